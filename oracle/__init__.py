@@ -1,0 +1,39 @@
+"""CPU oracle for paged-attention decode, chunked prefill and the KV-cache
+scatter.  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.
+
+It is a plain, slow, obviously correct float64 implementation of what the
+paged path computes: gather each sequence's K/V through its block table into
+contiguous arrays, then run dense softmax attention.  It shares no code with
+the HIP library or its binding; the only module both sides use is the seeded
+input generator (``paged_kv_cache_326_amd.synth``), which holds none of the
+method's arithmetic.
+
+Sources (web pages on paged KV caches):
+  [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践"
+       (seekfood.cn/news/1660747)
+  [P2] "KV Cache管理优化：大模型推理显存瓶颈突破"
+       (intelliparadigm.com/article/weixin_33178839/2255646)
+  [P3] "大语言模型KV Cache内存优化与PagedAttention实践"
+       (intelliparadigm.com/article/weixin_30558697/2223113)
+
+Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
+  kv_cache_bytes       the worked LLaMA-2-70B values printed on [P1]
+  blocks_needed        brute-force count of distinct blocks touched
+  slot_mapping         brute-force page-table walk + injectivity/ordering
+  reshape_and_cache    round trip, untouched-slot sentinel, skip/duplicate rules
+  decode_attention     torch SDPA (float64) on an identity-layout pool, closed
+                       forms, block-permutation and shared-prefix invariance
+  prefill_attention    torch SDPA causal / explicit-mask special cases
+No function here is "parity unpinned".
+"""
+
+from .storage import to_float64, round_to_storage  # noqa: F401
+from .paging import (  # noqa: F401
+    blocks_needed,
+    kv_cache_bytes,
+    slot_mapping,
+    reshape_and_cache,
+    gather_kv,
+)
+from .attention import decode_attention, prefill_attention  # noqa: F401

@@ -1,0 +1,106 @@
+"""Paging arithmetic of the oracle: block counts, KV size, slot mapping, the
+KV scatter into pool slots and the gather back out.  Test infrastructure only.
+
+Sources:
+  [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践"
+  [P2] "KV Cache管理优化：大模型推理显存瓶颈突破"
+  [P3] "大语言模型KV Cache内存优化与PagedAttention实践"
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    """Physical blocks a sequence of ``num_tokens`` tokens occupies.
+
+    [P1] "生产级推理引擎的内存管理与调度": the scheduler's block need is the
+    token count divided by the block size, rounded up (a partly filled last
+    block is still a whole block).
+    """
+    if num_tokens < 0 or block_size <= 0:
+        raise ValueError("negative token count or non-positive block size")
+    return (int(num_tokens) + int(block_size) - 1) // int(block_size)
+
+
+def kv_cache_bytes(
+    num_layers: int, seq_len: int, num_kv_heads: int, head_dim: int, dtype_size: int, batch_size: int
+) -> int:
+    """Bytes of K plus V for a batch.
+
+    [P1] "KV Cache 的内存开销与分页机制": the cache holds one key and one value
+    vector per layer, token, and KV head, each ``head_dim`` elements wide, for
+    every request of the batch; the factor 2 counts K and V.
+    """
+    return 2 * num_layers * seq_len * num_kv_heads * head_dim * dtype_size * batch_size
+
+
+def slot_mapping(
+    block_tables: np.ndarray, seq_lens: np.ndarray, q_lens: np.ndarray, block_size: int
+) -> np.ndarray:
+    """Pool slot of every new token, in sequence order.
+
+    [P1] "KV Cache 的内存开销与分页机制": a request's block table maps its
+    logical blocks to physical blocks; a token at position ``pos`` lives in
+    logical block ``pos // block_size`` at offset ``pos % block_size``, and the
+    new token of a step goes into the current (or a newly allocated) block.
+    A slot numbers the pool's token positions: physical block times the block
+    size plus the offset.  Sequence ``s`` writes ``q_lens[s]`` new tokens at
+    positions ``seq_lens[s] - q_lens[s]`` .. ``seq_lens[s] - 1`` (its length
+    counts this step's tokens).
+    """
+    block_tables = np.asarray(block_tables)
+    out = []
+    for s in range(len(seq_lens)):
+        L, q = int(seq_lens[s]), int(q_lens[s])
+        for pos in range(L - q, L):
+            logical = pos // block_size
+            physical = int(block_tables[s, logical])
+            out.append(physical * block_size + pos % block_size)
+    return np.asarray(out, dtype=np.int64)
+
+
+def reshape_and_cache(
+    key_cache: np.ndarray,
+    value_cache: np.ndarray,
+    key: np.ndarray,
+    value: np.ndarray,
+    slots: np.ndarray,
+) -> None:
+    """Write each new token's K and V (all KV heads) into its pool slot, in place.
+
+    Cache layout [num_blocks, num_kv_heads, block_size, head_dim]: within one
+    (block, KV head) the block's token vectors are contiguous, the layout that
+    lets in-block KV reads coalesce ([P1] "PagedAttention 的 CUDA Kernel 实现").
+    A negative slot marks a padding token and is skipped; two tokens may not
+    share a slot.  Values are copied bit for bit.
+    """
+    B = key_cache.shape[2]
+    slots = np.asarray(slots, dtype=np.int64)
+    valid = slots[slots >= 0]
+    if len(np.unique(valid)) != len(valid):
+        raise ValueError("two tokens map to the same slot")
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        block, offset = int(slot) // B, int(slot) % B
+        key_cache[block, :, offset, :] = key[t]
+        value_cache[block, :, offset, :] = value[t]
+
+
+def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndarray, seq_len: int):
+    """Contiguous K and V [seq_len, num_kv_heads, head_dim] of one sequence.
+
+    [P1] "PagedAttention 的 CUDA Kernel 实现": for each logical block, look up
+    its physical block ID in the block table, then read that block's vectors.
+    Only the first ``blocks_needed(seq_len)`` table entries are read, and of
+    the last block only the filled offsets.
+    """
+    B = key_cache.shape[2]
+    n = blocks_needed(seq_len, B)
+    phys = np.asarray(table_row[:n], dtype=np.int64)
+    # [n, Hkv, B, D] -> [n, B, Hkv, D] -> [n*B, Hkv, D]; logical order is block-major, offset-minor.
+    K = key_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, key_cache.shape[1], key_cache.shape[3])
+    V = value_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, value_cache.shape[1], value_cache.shape[3])
+    return K[:seq_len], V[:seq_len]
