@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Paged-decode benchmark on one MI355X.
+
+One step is the whole hot path over one batch: slot mapping of the new
+tokens, the KV scatter into the pool, then decode attention over every
+sequence's paged K/V (partition kernel + merge).  The default workload is one
+LLaMA-2-70B-shaped layer: 16 sequences x 4096 tokens, 64 query / 8 KV heads,
+head_dim 128, fp16, block size 16, a randomly permuted pool of 4096 blocks.
+
+Inputs are resident in HBM before timing.  Three copies of the pool (and of
+every per-step tensor) are rotated so that successive steps cannot be served
+from the 256 MB last-level cache.
+
+Prints one JSON line.  ``value`` is attended KV tokens per second for the
+whole step; ``roofline`` reports the decode call's algorithmic bytes over
+its event-timed duration against 8 TB/s; ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_decode_bytes(w) -> int:
+    """K+V of every attended token, query in, output out, the block-table
+    entries actually read, and seq_lens."""
+    dt = w.elem_bytes
+    B = w.block_size
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * dt * 2
+    qo = 2 * w.num_seqs * w.num_heads * w.head_dim * dt
+    bt = int(sum(-(-int(L) // B) for L in w.seq_lens)) * 4
+    return kv + qo + bt + 4 * w.num_seqs
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the oracle (as it stands) on this host: scatter + decode of the
+    whole batch, repeated until `budget_s` has elapsed (at least once)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    dt = w.dtype
+    q = oracle.to_float64(w.query, dt)
+    nk = oracle.to_float64(w.new_key, dt)
+    nv = oracle.to_float64(w.new_value, dt)
+    kc0 = oracle.to_float64(w.key_cache, dt)
+    vc0 = oracle.to_float64(w.value_cache, dt)
+    reps, spent = 0, 0.0
+    while reps == 0 or spent < budget_s:
+        kc, vc = kc0.copy(), vc0.copy()
+        t0 = time.perf_counter()
+        slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
+        oracle.reshape_and_cache(kc, vc, nk, nv, slots)
+        oracle.decode_attention(q, kc, vc, w.block_tables, w.seq_lens, w.scale)
+        spent += time.perf_counter() - t0
+        reps += 1
+    toks = int(w.seq_lens.sum()) * reps
+    return {
+        "value": toks / spent,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{reps} full step(s) of the same workload (slot mapping, scatter, float64 decode of all "
+                  f"{w.num_seqs} sequences) in {spent:.1f} s; host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..4 (decode configs)")
+    ap.add_argument("--partition", type=int, default=0, help="decode partition length (0 = automatic)")
+    ap.add_argument("--copies", type=int, default=3, help="rotated pool copies")
+    ap.add_argument("--identity-tables", action="store_true", help="unpermuted block layout (indirection overhead)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the decode shards by "
+              "sequence or KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_326_amd import pa, synth
+    from tests import harness
+
+    if not os.path.exists(os.path.join(ROOT, "paged_kv_cache_326_amd", "libpa.so")):
+        from paged_kv_cache_326_amd import build
+
+        build.build()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = synth.config(args.config, poison_unused=False)
+    if args.identity_tables:
+        w = synth.identity_tables(w)
+    P = args.partition or pa.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, w.max_seq_len, w.block_size)
+    copies = [harness.GpuWorkload(w)]
+    for _ in range(args.copies - 1):
+        g = harness.GpuWorkload.__new__(harness.GpuWorkload)
+        g.__dict__.update({k: (v.clone() if torch.is_tensor(v) else v) for k, v in copies[0].__dict__.items()})
+        copies.append(g)
+    ws = [pa.decode_workspace(c.query, c.key_cache, w.max_seq_len, P) for c in copies]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = copies[i % len(copies)]
+        c.slots()
+        c.scatter()
+        if ev is not None:
+            ev[0].record(stream)
+        c.decode(partition_size=P, workspace=ws[i % len(copies)])
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = total_ms / args.steps
+    dec_avg_s = float(dec_ms.mean()) * 1e-3
+
+    attended = int(w.seq_lens.sum())
+    nbytes = algorithmic_decode_bytes(w)
+    achieved = nbytes / dec_avg_s / 1e9
+    rec = {
+        "metric": "paged decode achieved HBM GB/s (% of peak) and attended KV tokens/sec, 1 GPU",
+        "value": attended / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "seq_lens": "all %d" % w.max_seq_len if len(set(w.seq_lens.tolist())) == 1 else
+                        "mixed, sum %d, max %d" % (attended, w.max_seq_len),
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "block_tables": "identity" if args.identity_tables else "random permutation",
+            "partition": P,
+            "pool_copies": len(copies),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (partition + merge kernels)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes": nbytes,
+            "decode_us_mean": float(dec_ms.mean()) * 1e3,
+            "decode_us_median": float(np.median(dec_ms)) * 1e3,
+            "decode_us_p10": float(np.percentile(dec_ms, 10)) * 1e3,
+            "decode_us_p90": float(np.percentile(dec_ms, 90)) * 1e3,
+        },
+        "attended_kv_tokens_per_s_decode": attended / dec_avg_s,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache attention for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources (web pages on paged KV caches):
+ *   [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践"
+ *        (seekfood.cn/news/1660747)
+ *   [P2] "KV Cache管理优化：大模型推理显存瓶颈突破"
+ *        (intelliparadigm.com/article/weixin_33178839/2255646)
+ *
+ * Memory model.  Every pointer argument except `cache` (a host struct) is a
+ * DEVICE pointer owned by the caller; the library never allocates, frees or
+ * synchronises.  Arrays are dense and row-major.  Work is enqueued on
+ * `stream` (0 = the legacy default stream) and runs asynchronously: the
+ * caller synchronises before reading results.
+ *
+ * KV pool ([P1] "KV Cache 的内存开销与分页机制", fixed-size physical blocks;
+ * [P2] section 2.1, one pool preallocated up front).  One layer's pool is two
+ * arrays of identical shape
+ *     key_cache, value_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ * so that the block_size token vectors of one (block, KV head) are one
+ * contiguous tile ([P1] "PagedAttention 的 CUDA Kernel 实现": vectors of a
+ * block sit together so that reads coalesce).  A slot numbers token positions
+ * in the pool: slot = physical_block * block_size + offset.
+ *
+ * Block tables ([P1] "KV Cache 的内存开销与分页机制": one table per request,
+ * logical block -> physical block) are int32 [num_seqs][max_blocks_per_seq];
+ * only the first ceil(seq_len / block_size) entries of a row are read.
+ *
+ * seq_lens counts the tokens a sequence holds in the pool INCLUDING the
+ * tokens written this step (so a decode token attends to itself).
+ *
+ * Errors.  Argument checks run on the host before anything is enqueued; on
+ * failure nothing is launched and outputs are untouched.  A failed launch
+ * returns PA_ERR_LAUNCH.  Device-resident contents (block IDs, seq_lens,
+ * slots) are the caller's contract; kernels nonetheless skip block IDs
+ * outside [0, num_blocks), slots outside the pool, and clamp seq_lens to the
+ * host-side bounds, so a bad table gives a wrong result, never an
+ * out-of-bounds access.
+ *
+ * Supported: head_dim in {64, 128}; block_size in {16, 32};
+ * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype f32, f16, bf16
+ * (prefill: f16, bf16).
+ *
+ * Thread safety: no global mutable state; calls on different streams may run
+ * concurrently as long as their output buffers do not overlap.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. num_heads % num_kv_heads != 0) */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim / block_size / dtype / group size not built */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
+  PA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+/* One layer's paged KV pool.  Both arrays are device memory owned by the
+ * caller, shape [num_blocks][num_kv_heads][block_size][head_dim], `dtype`. */
+typedef struct {
+  void* key_cache;
+  void* value_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  pa_dtype dtype;
+} pa_kv_cache;
+
+/* Slot of every new token.  [P1] "KV Cache 的内存开销与分页机制": a token at
+ * position pos of sequence s lives in logical block pos / block_size at offset
+ * pos % block_size; a step's new tokens go into the current (or a freshly
+ * appended) block of the table.
+ *
+ * block_tables  int32 [num_seqs][max_blocks_per_seq]
+ * seq_lens      int32 [num_seqs], tokens after this step
+ * cu_q_lens     int32 [num_seqs + 1], prefix sums of new-token counts
+ *               (sequence s writes positions seq_lens[s] - q_s .. seq_lens[s] - 1)
+ * slot_mapping  int64 [num_tokens] out, num_tokens = cu_q_lens[num_seqs];
+ *               slot = block_tables[s][pos / block_size] * block_size
+ *                      + pos % block_size, or -1 when pos is negative or its
+ *               logical block is beyond max_blocks_per_seq.
+ */
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, const int32_t* cu_q_lens,
+                          int32_t num_seqs, int32_t block_size,
+                          int64_t* slot_mapping, int32_t num_tokens,
+                          hipStream_t stream);
+
+/* Scatter new tokens' K and V into their pool slots (bit-exact copy).
+ * [P1] "KV Cache 的内存开销与分页机制": the new token's vectors are stored in
+ * the current block, or in a block appended to the table when it is full.
+ *
+ * key, value    [num_tokens][num_kv_heads][head_dim], cache->dtype
+ * slot_mapping  int64 [num_tokens]; a negative slot marks a padding token and
+ *               is skipped.  Two tokens must not share a slot.
+ */
+pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const void* value,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               hipStream_t stream);
+
+/* Partition length (tokens) that pa_decode picks when partition_size is 0. */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                 int32_t block_size);
+
+/* Bytes of float32 scratch pa_decode needs to keep per-partition softmax
+ * statistics and partial outputs of sequences longer than one partition.
+ * partition_size 0 means the automatic choice (pass the same value to the
+ * decode call).  Returns 0 on invalid arguments. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size);
+
+/* Decode attention over the paged cache: one query token per sequence.
+ * [P1] "PagedAttention 的 CUDA Kernel 实现": for each logical block, look up
+ * the physical block in the table and read its K/V vectors; [P1]
+ * "工程边界与架构取舍": decode reads the whole cache of a sequence for one
+ * token.  Computes, for every query head h of KV group g = h / (num_heads /
+ * num_kv_heads),
+ *     out[s][h] = softmax_t(scale * q[s][h] . K[s][t][g]) . V[s][t][g],
+ * t over 0 .. seq_lens[s]-1; a sequence of length 0 yields zeros.
+ *
+ * out, query    [num_seqs][num_heads][head_dim], cache->dtype (out is
+ *               rounded from float32 to nearest-even)
+ * max_seq_len   host-side upper bound of seq_lens (<= max_blocks_per_seq *
+ *               block_size); longer device values are clamped to it
+ * workspace     device scratch of at least pa_decode_workspace_bytes(); may
+ *               be NULL when that size is 0.  Overwritten; must not overlap
+ *               out, query or the cache.
+ */
+pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t max_seq_len, float scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* pa_decode with an explicit partition length in tokens: a positive multiple
+ * of block_size no larger than 1024 (0 = automatic). */
+pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_seq_len, float scale, void* workspace,
+                       size_t workspace_bytes, int32_t partition_size, hipStream_t stream);
+
+const char* pa_status_string(pa_status status);
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,170 @@
+// C ABI of libpa.so: host-side argument checks, partition choice, workspace
+// layout and dispatch to the gfx950 kernels.  Every check runs before any
+// launch; a failed check launches nothing.
+#include "../../include/pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kCUs = 256;  // MI355X compute units
+
+bool supported_shape(int head_dim, int block_size) {
+  return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+bool supported_group(int num_heads, int num_kv_heads) {
+  if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads) return false;
+  const int g = num_heads / num_kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+pa_status check_cache(const pa_kv_cache* c) {
+  if (!c || !c->key_cache || !c->value_cache) return PA_ERR_NULL;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (!supported_shape(c->head_dim, c->block_size)) return PA_ERR_UNSUPPORTED;
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa::KvCacheArgs to_args(const pa_kv_cache* c) {
+  pa::KvCacheArgs a;
+  a.key_cache = c->key_cache;
+  a.value_cache = c->value_cache;
+  a.num_blocks = c->num_blocks;
+  a.num_kv_heads = c->num_kv_heads;
+  a.head_dim = c->head_dim;
+  a.block_size = c->block_size;
+  a.dtype = static_cast<pa::DType>(c->dtype);
+  return a;
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t m_off, l_off, o_off, bytes;
+};
+
+WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int num_partitions) {
+  const size_t rows = (size_t)num_seqs * num_heads * num_partitions;
+  WsLayout w;
+  w.m_off = 0;
+  w.l_off = align256(rows * 4);
+  w.o_off = w.l_off + align256(rows * 4);
+  w.bytes = w.o_off + align256(rows * head_dim * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or head grouping";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* pa_version(void) { return "pa-mi355x 0.1.0 (gfx950)"; }
+
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size, int64_t* slot_mapping,
+                          int32_t num_tokens, hipStream_t stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0 || block_size <= 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!block_tables || !seq_lens || !cu_q_lens || !slot_mapping) return PA_ERR_NULL;
+  const hipError_t e = pa::launch_slot_mapping(block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, num_seqs,
+                                               block_size, slot_mapping, num_tokens, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const void* value,
+                               const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  const hipError_t e = pa::launch_reshape_and_cache(to_args(cache), key, value, slot_mapping, num_tokens, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {
+  // Aim for at least four workgroups per compute unit; longer partitions
+  // amortise the merge, shorter ones fill the chip when there are few
+  // (sequence, KV head) pairs.
+  if (block_size <= 0) return 0;
+  const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  int p = 512;
+  while (p > 128 && pairs * ceil_div(max_seq_len > 0 ? max_seq_len : 1, p) < 4 * kCUs) p /= 2;
+  if (p < block_size) p = block_size;
+  return p - p % block_size;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_seq_len < 0) return 0;
+  int p = partition_size;
+  if (p == 0) p = pa_decode_auto_partition(num_seqs, num_kv_heads, max_seq_len, block_size);
+  if (p <= 0 || max_seq_len <= p) return 0;
+  return ws_layout(num_seqs, num_heads, head_dim, ceil_div(max_seq_len, p)).bytes;
+}
+
+pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                       int32_t partition_size, hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!supported_group(num_heads, cache->num_kv_heads)) {
+    return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  }
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
+  int p = partition_size;
+  if (p == 0) p = pa_decode_auto_partition(num_seqs, cache->num_kv_heads, max_seq_len, cache->block_size);
+  if (p <= 0 || p % cache->block_size || p > pa::kMaxPartition) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !block_tables || !seq_lens) return PA_ERR_NULL;
+
+  pa::DecodeArgs a{};
+  a.cache = to_args(cache);
+  a.out = out;
+  a.query = query;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.partition = p;
+  a.num_partitions = max_seq_len > 0 ? ceil_div(max_seq_len, p) : 1;
+  if (max_seq_len > p) {
+    const WsLayout wl = ws_layout(num_seqs, num_heads, cache->head_dim, a.num_partitions);
+    if (!workspace || workspace_bytes < wl.bytes) return PA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(base + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
+    a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
+  }
+  const hipError_t e = pa::launch_decode(a, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return pa_decode_ex(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads,
+                      max_seq_len, scale, workspace, workspace_bytes, 0, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Slot mapping and the KV scatter into the paged pool (gfx950).
+//
+// Sources: [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践",
+// section "KV Cache 的内存开销与分页机制" (block table maps logical to
+// physical blocks; a new token goes into the current block or a new one).
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// One workgroup per sequence; its threads walk that sequence's new tokens.
+__global__ void __launch_bounds__(256) slot_mapping_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_blocks, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q_lens, int32_t block_size, int64_t* __restrict__ slots,
+    int32_t num_tokens) {
+  const int s = blockIdx.x;
+  const int t0 = cu_q_lens[s];
+  const int t1 = cu_q_lens[s + 1];
+  const int L = seq_lens[s];
+  const int q = t1 - t0;
+  for (int i = threadIdx.x; i < q; i += blockDim.x) {
+    const int t = t0 + i;
+    if (t < 0 || t >= num_tokens) continue;
+    const int pos = L - q + i;
+    int64_t slot = -1;
+    if (pos >= 0) {
+      const int logical = pos / block_size;
+      if (logical < max_blocks) {
+        const int64_t phys = block_tables[(int64_t)s * max_blocks + logical];
+        slot = phys * block_size + pos % block_size;
+      }
+    }
+    slots[t] = slot;
+  }
+}
+
+// Each thread moves one 16-byte chunk of one token's K or V row.  A token row
+// of one KV head is head_dim elements; the pool tile of (block, KV head) is
+// [block_size][head_dim], so the destination of (token, head) is
+//   ((block * num_kv_heads + head) * block_size + offset) * head_dim.
+template <typename T>
+__global__ void __launch_bounds__(256) reshape_and_cache_kernel(
+    T* __restrict__ key_cache, T* __restrict__ value_cache, const T* __restrict__ key,
+    const T* __restrict__ value, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t pool_slots) {
+  constexpr int VEC = vec16<T>();
+  const int chunks_per_row = head_dim / VEC;          // 16-byte chunks per head row
+  const int chunks_per_tok = num_kv_heads * chunks_per_row;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * chunks_per_tok * 2;
+  if (gid >= total) return;
+  const int which = (int)(gid / ((int64_t)num_tokens * chunks_per_tok));  // 0 = K, 1 = V
+  const int64_t rem = gid - (int64_t)which * num_tokens * chunks_per_tok;
+  const int t = (int)(rem / chunks_per_tok);
+  const int c = (int)(rem % chunks_per_tok);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int h = c / chunks_per_row;
+  const int ch = c % chunks_per_row;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot % block_size);
+  const T* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
+  T* dst = (which ? value_cache : key_cache) +
+           ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
+  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                               const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
+                               int64_t* slots, int32_t num_tokens, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, block_tables, max_blocks,
+                     seq_lens, cu_q_lens, block_size, slots, num_tokens);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_rac(const KvCacheArgs& c, const void* key, const void* value, const int64_t* slots,
+                             int32_t num_tokens, hipStream_t stream) {
+  constexpr int VEC = vec16<T>();
+  const int64_t total = (int64_t)num_tokens * c.num_kv_heads * (c.head_dim / VEC) * 2;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (T*)c.key_cache, (T*)c.value_cache, (const T*)key, (const T*)value, slots, num_tokens,
+                     c.num_kv_heads, c.head_dim, c.block_size, (int64_t)c.num_blocks * c.block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const KvCacheArgs& c, const void* key, const void* value,
+                                    const int64_t* slots, int32_t num_tokens, hipStream_t stream) {
+  switch (c.dtype) {
+    case DType::kF32:
+      return launch_rac<float>(c, key, value, slots, num_tokens, stream);
+    case DType::kF16:
+      return launch_rac<f16_t>(c, key, value, slots, num_tokens, stream);
+    case DType::kBF16:
+      return launch_rac<bf16_t>(c, key, value, slots, num_tokens, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,123 @@
+// Device helpers shared by the gfx950 kernels of libpa.so: storage dtypes,
+// 16-byte vector types, conversions and wave64 cross-lane primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Storage element types.  bf16 is carried as raw 16-bit patterns so every
+// conversion below is explicit.
+struct bf16_t {
+  uint16_t bits;
+};
+typedef _Float16 f16_t;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct Elem<f16_t> {
+  static constexpr int kBytes = 2;
+};
+template <>
+struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+
+// Elements of T per 16-byte load.
+template <typename T>
+constexpr int vec16() {
+  return 16 / Elem<T>::kBytes;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// float32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Unpack one 32-bit word holding two storage elements (or one f32) to floats.
+template <typename T>
+__device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b);
+template <>
+__device__ __forceinline__ void unpack2<f16_t>(uint32_t w, float& a, float& b) {
+  a = f16_lo(w);
+  b = f16_hi(w);
+}
+template <>
+__device__ __forceinline__ void unpack2<bf16_t>(uint32_t w, float& a, float& b) {
+  a = bf16_lo(w);
+  b = bf16_hi(w);
+}
+
+// Store one float as a storage element.
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, float x);
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, float x) {
+  *p = x;
+}
+template <>
+__device__ __forceinline__ void store_elem<f16_t>(f16_t* p, float x) {
+  *p = (_Float16)x;  // v_cvt_f16_f32 rounds to nearest-even
+}
+template <>
+__device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) {
+  p->bits = f32_to_bf16_bits(x);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves.  DPP works inside 16-lane rows; the controls used here:
+//   quad_perm xor 1 / xor 2  (within groups of 4 lanes)
+//   row_half_mirror          (lane i <-> 7 - i inside each group of 8)
+//   row_ror:8                (lane i <-> i ^ 8 inside each row of 16)
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,   // row_half_mirror
+  kDppRowRor8 = 0x128,      // row_ror:8
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,47 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct KvCacheArgs {
+  void* key_cache;
+  void* value_cache;
+  int32_t num_blocks, num_kv_heads, head_dim, block_size;
+  DType dtype;
+};
+
+struct DecodeArgs {
+  KvCacheArgs cache;
+  void* out;
+  const void* query;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t num_seqs, num_heads, max_seq_len;
+  float scale;
+  int32_t partition;      // tokens per partition, multiple of block_size
+  int32_t num_partitions; // ceil(max_seq_len / partition)
+  float* ws_m;            // [num_seqs][num_heads][num_partitions]
+  float* ws_l;            // same
+  float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]
+};
+
+constexpr int kMaxPartition = 1024;
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                               const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
+                               int64_t* slots, int32_t num_tokens, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const KvCacheArgs& c, const void* key, const void* value,
+                                    const int64_t* slots, int32_t num_tokens, hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

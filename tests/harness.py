@@ -1,0 +1,144 @@
+"""Test/benchmark plumbing: move seeded workloads to the GPU, run the HIP
+path through the C-ABI binding, and run the CPU oracle on the same inputs.
+The two paths meet only here, in the comparison."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_326_amd import synth  # noqa: E402
+
+# Unit roundoff of each output storage dtype (round to nearest).
+UNIT_ROUNDOFF = {"f32": 2.0**-24, "f16": 2.0**-11, "bf16": 2.0**-8}
+ATOL = RTOL = 2e-3
+
+
+def tolerance_ok(got64: np.ndarray, ref64: np.ndarray, dtype: str):
+    """|got - ref| <= ATOL + (RTOL + u_dtype) |ref| elementwise.
+
+    The 2e-3 absolute/relative bar covers the fp32 accumulation; the output is
+    then rounded to its storage dtype, which adds at most u_dtype |ref|.
+    """
+    err = np.abs(got64 - ref64)
+    bound = ATOL + (RTOL + UNIT_ROUNDOFF[dtype]) * np.abs(ref64)
+    bad = ~(err <= bound)  # NaN counts as bad
+    return (not bad.any()), float(np.nanmax(err) if err.size else 0.0), int(bad.sum())
+
+
+def build_if_missing():
+    from paged_kv_cache_326_amd import build
+
+    if not os.path.exists(build.LIB):
+        build.build()
+
+
+# --------------------------------------------------------------------------
+# GPU side
+# --------------------------------------------------------------------------
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    import torch
+
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float16))
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)
+
+
+def from_device(t, dtype: str) -> np.ndarray:
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class GpuWorkload:
+    """A workload's tensors on the GPU."""
+
+    def __init__(self, w: synth.Workload, device="cuda"):
+        import torch
+
+        self.w = w
+        dt = w.dtype
+        self.key_cache = to_device(w.key_cache, dt, device)
+        self.value_cache = to_device(w.value_cache, dt, device)
+        self.new_key = to_device(w.new_key, dt, device)
+        self.new_value = to_device(w.new_value, dt, device)
+        self.query = to_device(w.query, dt, device)
+        self.block_tables = torch.from_numpy(np.ascontiguousarray(w.block_tables, np.int32)).to(device)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(device)
+        self.cu_q_lens = torch.from_numpy(np.ascontiguousarray(w.cu_q_lens, np.int32)).to(device)
+        self.out = torch.empty_like(self.query)
+        self.slot_mapping = torch.empty(w.num_new_tokens, dtype=torch.int64, device=device)
+
+    def slots(self):
+        from paged_kv_cache_326_amd import pa
+
+        pa.pa_slot_mapping(self.block_tables, self.seq_lens, self.cu_q_lens, self.w.block_size, self.slot_mapping)
+        return self.slot_mapping
+
+    def scatter(self):
+        from paged_kv_cache_326_amd import pa
+
+        pa.pa_reshape_and_cache(self.key_cache, self.value_cache, self.new_key, self.new_value, self.slot_mapping)
+
+    def decode(self, partition_size=0, workspace=None):
+        from paged_kv_cache_326_amd import pa
+
+        pa.pa_decode(self.out, self.query, self.key_cache, self.value_cache, self.block_tables, self.seq_lens,
+                     self.w.scale, self.w.max_seq_len, workspace=workspace, partition_size=partition_size)
+        return self.out
+
+    def step(self, partition_size=0):
+        """slot mapping -> scatter -> decode, all on the current stream."""
+        self.slots()
+        self.scatter()
+        return self.decode(partition_size)
+
+
+# --------------------------------------------------------------------------
+# Oracle side
+# --------------------------------------------------------------------------
+
+
+def oracle_step(w: synth.Workload, seqs=None):
+    """Oracle slots, scattered float64 caches, and decode output for `seqs`."""
+    import oracle
+
+    dt = w.dtype
+    kc = oracle.to_float64(w.key_cache, dt)
+    vc = oracle.to_float64(w.value_cache, dt)
+    slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
+    oracle.reshape_and_cache(kc, vc, oracle.to_float64(w.new_key, dt), oracle.to_float64(w.new_value, dt), slots)
+    idx = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs)
+    q = oracle.to_float64(w.query, dt)
+    out = oracle.decode_attention(q[idx], kc, vc, w.block_tables[idx], w.seq_lens[idx], w.scale)
+    return slots, kc, vc, out
+
+
+def oracle_scatter_storage(w: synth.Workload):
+    """The pool after the oracle's scatter, in storage representation (for a
+    byte-exact comparison).  The oracle copies values bit for bit, so doing
+    it on the storage arrays is the same operation."""
+    import oracle
+
+    kc = w.key_cache.copy()
+    vc = w.value_cache.copy()
+    slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
+    oracle.reshape_and_cache(kc, vc, w.new_key, w.new_value, slots)
+    return slots, kc, vc

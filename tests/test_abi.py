@@ -1,0 +1,100 @@
+"""The C ABI library loads, exports everything include/pa.h declares, and
+rejects bad arguments on the host before any launch.  CPU only: no call here
+reaches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests import harness
+
+ROOT = harness.ROOT
+
+
+@pytest.fixture(scope="module")
+def L():
+    harness.build_if_missing()
+    from paged_kv_cache_326_amd import pa
+
+    return pa.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "pa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert "pa_decode" in names and "pa_reshape_and_cache" in names
+    for n in names:
+        assert hasattr(L, n), f"libpa.so does not export {n}"
+    from paged_kv_cache_326_amd import pa
+
+    assert set(pa.EXPORTS) <= set(names)
+
+
+def test_version_and_status_strings(L):
+    assert b"gfx950" in L.pa_version()
+    for s in range(6):
+        assert L.pa_status_string(s)
+
+
+def _cache(pa, **kw):
+    c = pa.pa_kv_cache(0x1000, 0x2000, 64, 2, 64, 16, pa.PA_F16)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _decode(L, pa, c, **kw):
+    a = dict(out=0x3000, query=0x4000, bt=0x5000, mb=4, sl=0x6000, S=4, Hq=8, maxL=50, scale=0.125,
+             ws=0x7000, wsb=1 << 20, P=0)
+    a.update(kw)
+    return L.pa_decode_ex(ctypes.byref(c), a["out"], a["query"], a["bt"], a["mb"], a["sl"], a["S"], a["Hq"], a["maxL"],
+                          a["scale"], a["ws"], a["wsb"], a["P"], None)
+
+
+def test_decode_argument_errors(L):
+    from paged_kv_cache_326_amd import pa
+
+    assert _decode(L, pa, _cache(pa, key_cache=0)) == 1  # NULL cache array
+    assert _decode(L, pa, _cache(pa), query=0) == 1
+    assert _decode(L, pa, _cache(pa, head_dim=96)) == 3  # unsupported head_dim
+    assert _decode(L, pa, _cache(pa, block_size=8)) == 3
+    assert _decode(L, pa, _cache(pa, dtype=7)) == 3
+    assert _decode(L, pa, _cache(pa), Hq=7) == 2  # not a multiple of num_kv_heads
+    assert _decode(L, pa, _cache(pa), Hq=32) == 3  # group of 16 not built
+    assert _decode(L, pa, _cache(pa), maxL=65) == 2  # beyond max_blocks_per_seq * block_size
+    assert _decode(L, pa, _cache(pa), P=24) == 2  # not a multiple of block_size
+    assert _decode(L, pa, _cache(pa), P=2048) == 2
+    assert _decode(L, pa, _cache(pa), P=16, ws=0) == 4  # needs a workspace
+    assert _decode(L, pa, _cache(pa), P=16, wsb=100) == 4
+    assert _decode(L, pa, _cache(pa), S=0) == 0  # nothing to do, nothing launched
+
+
+def test_workspace_size_formula(L):
+    # 4 sequences x 8 heads x ceil(50/16)=4 partitions: m and l rows (float32,
+    # 256-byte aligned) plus head_dim floats per row.
+    rows = 4 * 8 * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 16) == 2 * al(rows * 4) + al(rows * 64 * 4)
+    assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 64) == 0  # one partition: written directly
+    assert L.pa_decode_auto_partition(16, 8, 4096, 16) in (128, 256, 512)
+    assert L.pa_decode_auto_partition(16, 8, 4096, 16) % 16 == 0
+
+
+def test_scatter_and_slot_argument_errors(L):
+    from paged_kv_cache_326_amd import pa
+
+    c = _cache(pa)
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0, 0x10, 0x20, 4, None) == 1
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0x10, 0x10, 0x20, -1, None) == 2
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0x10, 0x10, 0x20, 0, None) == 0
+    assert L.pa_reshape_and_cache(ctypes.byref(_cache(pa, num_blocks=0)), 0x10, 0x10, 0x20, 4, None) == 2
+    assert L.pa_slot_mapping(0x10, 4, 0x20, 0x30, 4, 0, 0x40, 4, None) == 2
+    assert L.pa_slot_mapping(0x10, 4, 0, 0x30, 4, 16, 0x40, 4, None) == 1
+    assert L.pa_slot_mapping(0x10, 4, 0x20, 0x30, 0, 16, 0x40, 0, None) == 0
