@@ -51,17 +51,22 @@ __device__ __forceinline__ float dot16(const u32x4& q, const u32x4& k, float acc
 template <>
 __device__ __forceinline__ float dot16<f16_t>(const u32x4& q, const u32x4& k, float acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]), __builtin_bit_cast(f16x2, k[i]), acc, false);
+  for (int i = 0; i < 4; ++i) {
+    // Copy the lane out of the vector first: bit-casting a vector element
+    // lvalue in place reads the vector's first element.
+    const uint32_t qi = q[i], ki = k[i];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qi), __builtin_bit_cast(f16x2, ki), acc, false);
+  }
   return acc;
 }
 
 template <>
 __device__ __forceinline__ float dot16<bf16_t>(const u32x4& q, const u32x4& k, float acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(i16x2, q[i]), __builtin_bit_cast(i16x2, k[i]), acc,
-                                          false);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t qi = q[i], ki = k[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(i16x2, qi), __builtin_bit_cast(i16x2, ki), acc, false);
+  }
   return acc;
 }
 

@@ -125,7 +125,7 @@ def oracle_step(w: synth.Workload, seqs=None):
     vc = oracle.to_float64(w.value_cache, dt)
     slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
     oracle.reshape_and_cache(kc, vc, oracle.to_float64(w.new_key, dt), oracle.to_float64(w.new_value, dt), slots)
-    idx = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs)
+    idx = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs, dtype=np.int64)
     q = oracle.to_float64(w.query, dt)
     out = oracle.decode_attention(q[idx], kc, vc, w.block_tables[idx], w.seq_lens[idx], w.scale)
     return slots, kc, vc, out
