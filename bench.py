@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="rotated pool copies")
     ap.add_argument("--identity-tables", action="store_true", help="unpermuted block layout (indirection overhead)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead: run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -111,6 +113,17 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "copies": args.steps}))
+        return
 
     w = synth.config(args.config, poison_unused=False)
     if args.identity_tables:

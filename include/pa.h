@@ -159,6 +159,31 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query,
                        int32_t max_seq_len, float scale, void* workspace,
                        size_t workspace_bytes, int32_t partition_size, hipStream_t stream);
 
+/* Chunked-prefill attention over the paged cache (causal).  [P1]
+ * "工程边界与架构取舍": prefill is a compute-bound matrix product and a long
+ * prompt is processed in chunks interleaved with decode steps; the chunk
+ * reads the cached prefix through the block table like decode does.
+ *
+ * Sequence s has q_s = cu_q_lens[s+1] - cu_q_lens[s] chunk tokens, already
+ * written to the pool (pa_reshape_and_cache), at positions ctx .. ctx+q_s-1
+ * with ctx = seq_lens[s] - q_s.  Chunk token i, head h attends to positions
+ * 0 .. ctx+i of KV head h / (num_heads / num_kv_heads):
+ *     out[t][h] = softmax_j(scale * q[t][h] . K[s][j]) . V[s][j],  j <= ctx+i.
+ *
+ * out, query   [cu_q_lens[num_seqs]][num_heads][head_dim], cache->dtype
+ *              (f16 or bf16; rounded to nearest-even)
+ * cu_q_lens    int32 [num_seqs + 1]
+ * seq_lens     int32 [num_seqs], >= the sequence's chunk length
+ * max_q_len    host-side upper bound of the chunk lengths
+ * Products run on v_mfma_f32_32x32x16 with fp32 accumulation; the softmax
+ * probabilities enter the PV product rounded to the cache dtype.
+ */
+pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* query,
+                           const int32_t* cu_q_lens, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, int32_t num_heads, int32_t max_q_len, float scale,
+                           hipStream_t stream);
+
 const char* pa_status_string(pa_status status);
 const char* pa_version(void);
 

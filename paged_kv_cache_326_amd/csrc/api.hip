@@ -167,4 +167,32 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query, cons
                       max_seq_len, scale, workspace, workspace_bytes, 0, stream);
 }
 
+pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* query, const int32_t* cu_q_lens,
+                           const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, int32_t num_heads, int32_t max_q_len, float scale, hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->dtype != PA_F16 && cache->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_q_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!supported_group(num_heads, cache->num_kv_heads)) {
+    return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  }
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !query || !cu_q_lens || !seq_lens || !block_tables) return PA_ERR_NULL;
+  pa::PrefillArgs a{};
+  a.cache = to_args(cache);
+  a.out = out;
+  a.query = query;
+  a.cu_q_lens = cu_q_lens;
+  a.seq_lens = seq_lens;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_qtiles = ceil_div(max_q_len, pa::prefill_positions_per_tile(num_heads / cache->num_kv_heads));
+  a.scale = scale;
+  const hipError_t e = pa::launch_prefill(a, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

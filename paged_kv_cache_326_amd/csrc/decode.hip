@@ -30,6 +30,8 @@
 //        M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -126,42 +128,98 @@ __device__ __forceinline__ float reduce_scatter8(float* a, int sub) {
   return a[0];
 }
 
+// LDS layout of one workgroup.  Each wave owns a logit/probability region
+// and a slot for its partial output; the block-table slice is shared.
 struct SmemLayout {
-  int bt_off, p_off, o_off, wmax_off, wsum_off, bytes;
+  int bt_off, p_off, p_wave, h_off, h_wave, o_off, m_off, l_off, bytes;
 };
 
 __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, int D) {
   SmemLayout s;
+  const int nblk = partition / B;
+  const int bpw = (nblk + kNW - 1) / kNW;  // blocks per wave
   int off = 0;
   s.bt_off = off;
-  off += ((partition / B) * 4 + 15) & ~15;
+  off += (nblk * 4 + 15) & ~15;
   s.p_off = off;
-  off += partition * G * 4;
+  s.p_wave = bpw * B * G;  // floats per wave
+  off += kNW * s.p_wave * 4;
+  s.h_off = off;
+  s.h_wave = bpw * B / 2 * G;  // dwords per wave: f16 probability pairs
+  off += kNW * s.h_wave * 4;
   s.o_off = off;
   off += kNW * G * D * 4;
-  s.wmax_off = off;
+  s.m_off = off;
   off += kNW * G * 4;
-  s.wsum_off = off;
+  s.l_off = off;
   off += kNW * G * 4;
   s.bytes = off;
   return s;
 }
 
+// Sum the per-lane PV accumulators x[NV] over the TS token slots of a wave
+// (the lanes that hold the same dims).  gfx950's row swaps do the first two
+// halvings: v_permlane32_swap exchanges the two 32-lane halves of a pair of
+// registers, v_permlane16_swap the odd rows of one with the even rows of the
+// other, so every swap-and-add halves the register count.  Afterwards lane
+// (row q, column c) holds full sums x[q * NV/R + j], j < NV/R, R = min(TS, 4),
+// rows counted in units of 64/R lanes; a third step (TS == 8) folds the two
+// slots that share a 16-lane row with a DPP rotate.
+template <int NV, int TS>
+__device__ __forceinline__ void reduce_slots(float* x) {
+  static_assert(TS == 2 || TS == 4 || TS == 8, "token slots");
+#pragma unroll
+  for (int j = 0; j < NV / 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j + NV / 2]), false, false);
+    x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (TS >= 4) {
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + NV / 4]), false, false);
+      x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (TS == 8) {
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) x[j] += dpp_mov<kDppRowRor8>(x[j]);
+  }
+}
+
+// Wave-local LDS ordering: the compiler may not move LDS accesses across this
+// point, and the wave's own earlier LDS writes are complete before later reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, int G>
+struct Occupancy {
+  // 2-byte types fit in 128 VGPRs (4 waves per SIMD); f32 is a correctness
+  // path and keeps the compiler's choice.
+  static constexpr int kWaves = Elem<T>::kBytes == 2 ? 4 : 1;
+};
+
 template <typename T, int D, int B, int G>
-__global__ void __launch_bounds__(kNW * 64) decode_partition_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(Occupancy<T, G>::kWaves)))
+decode_partition_kernel(DecodeArgs a) {
   constexpr int VEC = vec16<T>();
   constexpr int LPT = 8;            // lanes per token (QK)
   constexpr int DL = D / LPT;       // dims per lane (QK)
   constexpr int NCK = DL / VEC;     // 16-byte chunks per lane per token (QK)
+  constexpr int CH = 16;            // tokens per pipeline stage (a chunk; B is 16 or 32)
+  constexpr int CPB = B / CH;       // chunks per block
   constexpr int TPG = 64 / LPT;     // tokens per load group (QK)
-  constexpr int GPB = B / TPG;      // load groups per block (QK)
+  constexpr int GPC = CH / TPG;     // load groups per chunk (QK)
   constexpr int LPV = D / VEC;      // lanes per token (PV)
   constexpr int TS = 64 / LPV;      // token slots per load (PV)
-  constexpr int IPB = B / TS;       // loads per block (PV)
+  constexpr int IPC = CH / TS;      // loads per chunk (PV)
   constexpr int NT = kNW * 64;
   constexpr int SHIFT = 3 - Log2<G>::v;
-  static_assert(NCK >= 1 && GPB >= 1 && IPB >= 1, "unsupported shape");
-  static_assert(NT % G == 0, "thread count must be a multiple of the group size");
+  constexpr int NV = G * VEC;       // PV accumulators per lane
+  static_assert(B % CH == 0 && NCK >= 1 && GPC >= 1 && IPC >= 1, "unsupported shape");
+  static_assert(64 % G == 0, "group size must divide the wave");
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int part = blockIdx.x;
@@ -169,11 +227,6 @@ __global__ void __launch_bounds__(kNW * 64) decode_partition_kernel(DecodeArgs a
   const int s = blockIdx.z;
   const int P = a.partition;
   const SmemLayout lay = smem_layout(P, B, G, D);
-  int* s_bt = reinterpret_cast<int*>(smem + lay.bt_off);
-  float* s_p = reinterpret_cast<float*>(smem + lay.p_off);
-  float* s_o = reinterpret_cast<float*>(smem + lay.o_off);
-  float* s_wmax = reinterpret_cast<float*>(smem + lay.wmax_off);
-  float* s_wsum = reinterpret_cast<float*>(smem + lay.wsum_off);
 
   int L = a.seq_lens[s];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
@@ -188,6 +241,16 @@ __global__ void __launch_bounds__(kNW * 64) decode_partition_kernel(DecodeArgs a
   const int w = tid >> 6;
   const int Hkv = a.cache.num_kv_heads;
   const int Hq = a.num_heads;
+  int* s_bt = reinterpret_cast<int*>(smem + lay.bt_off);
+  float* s_p = reinterpret_cast<float*>(smem + lay.p_off) + w * lay.p_wave;
+  // f16 path: probabilities of token pairs (t, t + TS) packed as f16x2, one
+  // dword per (pair, head), pair index jc*CH/2 + (i/2)*TS + ts for the token
+  // loaded by PV load i of chunk jc in slot ts.
+  uint32_t* s_h = reinterpret_cast<uint32_t*>(smem + lay.h_off) + w * lay.h_wave;
+  constexpr bool kDot2PV = std::is_same<T, f16_t>::value;
+  float* s_o = reinterpret_cast<float*>(smem + lay.o_off);
+  float* s_m = reinterpret_cast<float*>(smem + lay.m_off);
+  float* s_l = reinterpret_cast<float*>(smem + lay.l_off);
 
   // 1. Block-table slice -> LDS.  Entries outside the pool become -1.
   {
@@ -215,130 +278,232 @@ __global__ void __launch_bounds__(kNW * 64) decode_partition_kernel(DecodeArgs a
   }
   __syncthreads();
 
-  const float qscale = a.scale * kLog2e;
-  const int myhead = sub >> SHIFT;
-  const bool writer = (sub & ((1 << SHIFT) - 1)) == 0;
+  // This wave's blocks: local index jl -> partition block w + jl*NW.
+  const int nbw = nblk > w ? (nblk - w + kNW - 1) / kNW : 0;
   const int64_t blk_stride = (int64_t)Hkv * B * D;
   const T* kbase = reinterpret_cast<const T*>(a.cache.key_cache) + (int64_t)g * B * D;
   const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * B * D;
+  const float qscale = a.scale * kLog2e;
+  const int myhead = sub >> SHIFT;
+  const bool writer = (sub & ((1 << SHIFT) - 1)) == 0;
 
-  // 2. QK.
+  // 2. QK with the next chunk's K in flight while the current one is used.
+  // Wave-local chunk jc is chunk jc % CPB of partition block w + (jc / CPB)*NW;
+  // its logits live at wave-local tokens jc*CH ...
+  const int nch = nbw * CPB;
   float run_max = -INFINITY;
-  for (int j = w; j < nblk; j += kNW) {
-    const int pb = s_bt[j];
-    if (pb < 0) {
-      if (writer)
-        for (int gi = 0; gi < GPB; ++gi) s_p[(j * B + gi * TPG + tq) * G + myhead] = -INFINITY;
-      continue;
+  auto chunk_src = [&](const T* base, int jc, int& t0) -> const T* {
+    const int jb = w + (jc / CPB) * kNW;
+    t0 = jb * B + (jc % CPB) * CH;  // first token of the chunk, partition-relative
+    const int pb = s_bt[jb];
+    return pb >= 0 ? base + pb * blk_stride + (jc % CPB) * CH * D : nullptr;
+  };
+  auto k_load = [&](u32x4 (&kb)[GPC][NCK], int jc) {
+    int t0;
+    const T* src = chunk_src(kbase, jc, t0);
+    if (src) {
+#pragma unroll
+      for (int gi = 0; gi < GPC; ++gi)
+#pragma unroll
+        for (int c = 0; c < NCK; ++c)
+          kb[gi][c] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(src + (gi * TPG + tq) * D + c * LPT * VEC + sub * VEC));
     }
-    const T* kb = kbase + pb * blk_stride;
-    u32x4 kv[GPB][NCK];
+  };
+  auto qk_block = [&](const u32x4 (&kb)[GPC][NCK], int jc) {
+    int t0;
+    const bool valid = chunk_src(kbase, jc, t0) != nullptr;
 #pragma unroll
-    for (int gi = 0; gi < GPB; ++gi)
-#pragma unroll
-      for (int c = 0; c < NCK; ++c)
-        kv[gi][c] = *reinterpret_cast<const u32x4*>(kb + (gi * TPG + tq) * D + c * LPT * VEC + sub * VEC);
-#pragma unroll
-    for (int gi = 0; gi < GPB; ++gi) {
+    for (int gi = 0; gi < GPC; ++gi) {
       float acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < NCK; ++c) x = dot16<T>(qv[h][c], kv[gi][c], x);
+        for (int c = 0; c < NCK; ++c) x = dot16<T>(qv[h][c], kb[gi][c], x);
         acc[h] = x;
       }
       float z = reduce_scatter8<G>(acc, sub);
-      const int tl = j * B + gi * TPG + tq;
-      z = tl < ntok ? z * qscale : -INFINITY;
+      const int tl = t0 + gi * TPG + tq;
+      z = (valid && tl < ntok) ? z * qscale : -INFINITY;
       run_max = fmaxf(run_max, z);
-      if (writer) s_p[tl * G + myhead] = z;
+      if (writer) s_p[(jc * CH + gi * TPG + tq) * G + myhead] = z;
+    }
+  };
+  {
+    u32x4 kb0[GPC][NCK], kb1[GPC][NCK];
+    if (nch > 0) k_load(kb0, 0);
+    for (int jc = 0; jc < nch; jc += 2) {
+      if (jc + 1 < nch) k_load(kb1, jc + 1);
+      qk_block(kb0, jc);
+      if (jc + 2 < nch) k_load(kb0, jc + 2);
+      if (jc + 1 < nch) qk_block(kb1, jc + 1);
     }
   }
-  // Per-wave, per-head maximum: lanes with equal `sub` hold the same head.
+
+  // The first V chunk goes out before the softmax so HBM stays busy.
+  auto v_load = [&](u32x4 (&vb)[IPC], int jc) {
+    int t0;
+    const T* src = chunk_src(vbase, jc, t0);
+    if (src) {
+      const int ts = lane / LPV, dc = lane % LPV;
+#pragma unroll
+      for (int i = 0; i < IPC; ++i)
+        vb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (i * TS + ts) * D + dc * VEC));
+    }
+  };
+  u32x4 vb0[IPC], vb1[IPC];
+  if (nch > 0) v_load(vb0, 0);
+
+  // 3. Wave-local softmax.  Lanes with equal `sub` hold the same head.
   run_max = fmaxf(run_max, shfl_xor(run_max, 8));
   run_max = fmaxf(run_max, shfl_xor(run_max, 16));
   run_max = fmaxf(run_max, shfl_xor(run_max, 32));
-  if (lane < LPT && writer) s_wmax[w * G + myhead] = run_max;
-  __syncthreads();
-
-  // 3. Softmax numerators and per-head sums.  NT % G == 0, so a thread always
-  // sees the same head.
-  const int hh = tid % G;
-  float M = -INFINITY;
-#pragma unroll
-  for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, s_wmax[ww * G + hh]);
+  // Lane `lane` now serves head lane % G (64 % G == 0): fetch that head's max.
+  const float M = __shfl(run_max, (lane % G) << SHIFT, 64);
+  wave_lds_sync();
   float lsum = 0.f;
   {
-    const int ne = nblk * B * G;
-    for (int e = tid; e < ne; e += NT) {
+    const int ne = nch * CH * G;
+    for (int e = lane; e < ne; e += 64) {
       const float z = s_p[e];
-      const float pr = z == -INFINITY ? 0.f : fast_exp2(z - M);
-      s_p[e] = pr;
+      float pr = z == -INFINITY ? 0.f : fast_exp2(z - M);
+      if constexpr (kDot2PV) {
+        // The PV product sees p rounded to f16; the normaliser sums the
+        // same rounded values.
+        const _Float16 ph = (_Float16)pr;
+        pr = (float)ph;
+        const int tw = e / G, hh = e % G;        // wave-local token, head
+        const int jc = tw / CH, tb = tw % CH;    // chunk, token within chunk
+        const int i = tb / TS, tsl = tb % TS;    // PV load index, slot
+        const int pair = jc * (CH / 2) + (i / 2) * TS + tsl;
+        reinterpret_cast<uint16_t*>(s_h)[(pair * G + hh) * 2 + (i & 1)] = __builtin_bit_cast(uint16_t, ph);
+      } else {
+        s_p[e] = pr;
+      }
       lsum += pr;
     }
   }
 #pragma unroll
   for (int m = G; m < 64; m <<= 1) lsum += shfl_xor(lsum, m);
-  if (lane < G) s_wsum[w * G + lane] = lsum;
-  __syncthreads();
+  wave_lds_sync();
 
-  // 4. PV.
+  // 4. PV, double-buffered like QK.
+  float o[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) o[k] = 0.f;
   const int ts = lane / LPV;
-  const int dc = lane % LPV;
-  float o[G][VEC];
+  auto pv_block = [&](const u32x4 (&vb)[IPC], int jc) {
+    int t0;
+    if (!chunk_src(vbase, jc, t0)) return;
+    if constexpr (kDot2PV) {
+      // Token pairs (load i, load i+1) of this slot: build (v_t0[d], v_t1[d])
+      // halves with v_perm and dot them with the packed (p_t0, p_t1).
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+      for (int i = 0; i < IPC; i += 2) {
+        u32x4 va = vb[i], vz = vb[i + 1];
+        // Tail of the last block: zero V of tokens past the end (p is 0
+        // there, and 0 * NaN would poison the sum).
+        if (t0 + i * TS + ts >= ntok) va = u32x4{0, 0, 0, 0};
+        if (t0 + (i + 1) * TS + ts >= ntok) vz = u32x4{0, 0, 0, 0};
+        uint32_t X[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) o[h][v] = 0.f;
-
-  for (int j = w; j < nblk; j += kNW) {
-    const int pb = s_bt[j];
-    if (pb < 0) continue;
-    const T* vb = vbase + pb * blk_stride;
-    u32x4 vv[IPB];
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = va[q], hi = vz[q];
+          X[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          X[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+        const int pair = jc * (CH / 2) + (i / 2) * TS + ts;
+        uint32_t pw[G];
+        const uint32_t* pp = s_h + pair * G;
+        if constexpr (G % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) vv[i] = *reinterpret_cast<const u32x4*>(vb + (i * TS + ts) * D + dc * VEC);
+          for (int h = 0; h < G; h += 4) {
+            const u32x4 v4 = *reinterpret_cast<const u32x4*>(pp + h);
+            pw[h] = v4[0], pw[h + 1] = v4[1], pw[h + 2] = v4[2], pw[h + 3] = v4[3];
+          }
+        } else {
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      const int tl = j * B + i * TS + ts;
-      if (tl >= ntok) continue;  // tail of the last block: never touch its (arbitrary) contents
+          for (int h = 0; h < G; ++h) pw[h] = pp[h];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const f16x2 ph = __builtin_bit_cast(f16x2, pw[h]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+            o[h * VEC + v] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(f16x2, X[v]), o[h * VEC + v], false);
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < IPC; ++i) {
+      const int tb = i * TS + ts;  // token within the chunk
+      if (t0 + tb >= ntok) continue;  // tail of the last block: never touch its contents
       float pr[G];
+      const float* pp = s_p + (jc * CH + tb) * G;
+      if constexpr (G % 4 == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) pr[h] = s_p[tl * G + h];
+        for (int h = 0; h < G; h += 4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(pp + h);
+          pr[h] = v4[0], pr[h + 1] = v4[1], pr[h + 2] = v4[2], pr[h + 3] = v4[3];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pr[h] = pp[h];
+      }
       float vf[VEC];
-      unpack16<T>(vv[i], vf);
+      unpack16<T>(vb[i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) o[h][v] = fmaf(pr[h], vf[v], o[h][v]);
+        for (int v = 0; v < VEC; ++v) o[h * VEC + v] = fmaf(pr[h], vf[v], o[h * VEC + v]);
+    }
+  };
+  for (int jc = 0; jc < nch; jc += 2) {
+    if (jc + 1 < nch) v_load(vb1, jc + 1);
+    pv_block(vb0, jc);
+    if (jc + 2 < nch) v_load(vb0, jc + 2);
+    if (jc + 1 < nch) pv_block(vb1, jc + 1);
+  }
+
+  // 5. Fold token slots, park the wave's partial in LDS, merge the waves.
+  reduce_slots<NV, TS>(o);
+  {
+    constexpr int R = TS < 4 ? TS : 4;
+    constexpr int PER = NV / R;  // values per lane after the fold
+    const int q = lane / (64 / R);
+    const int col = lane % (64 / R);
+    if (col < LPV) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int k = q * PER + j;
+        const int h = k / VEC, v = k % VEC;
+        s_o[(w * G + h) * D + col * VEC + v] = o[j];
+      }
     }
   }
-  // Sum the token slots of the wave (lanes that hold the same dims).
-#pragma unroll
-  for (int m = LPV; m < 64; m <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) o[h][v] += shfl_xor(o[h][v], m);
-  if (lane < LPV) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) s_o[(w * G + h) * D + dc * VEC + v] = o[h][v];
+  if (lane < G) {
+    s_m[w * G + lane] = M;
+    s_l[w * G + lane] = lsum;
   }
   __syncthreads();
 
-  // 5. Combine the waves; normalise and store, or park the partial.
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D;
     const int d = idx % D;
-    float acc = 0.f, l = 0.f, m = -INFINITY;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) {
-      acc += s_o[(ww * G + h) * D + d];
-      l += s_wsum[ww * G + h];
-      m = fmaxf(m, s_wmax[ww * G + h]);
+    for (int ww = 0; ww < kNW; ++ww) Mx = fmaxf(Mx, s_m[ww * G + h]);
+    float acc = 0.f, l = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kNW; ++ww) {
+        const float mw = s_m[ww * G + h];
+        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - Mx);
+        acc = fmaf(sc, s_o[(ww * G + h) * D + d], acc);
+        l = fmaf(sc, s_l[ww * G + h], l);
+      }
     }
     const int hq = g * G + h;
     if (direct) {
@@ -348,7 +513,7 @@ __global__ void __launch_bounds__(kNW * 64) decode_partition_kernel(DecodeArgs a
       const int64_t row = ((int64_t)s * Hq + hq) * a.num_partitions + part;
       a.ws_o[row * D + d] = acc;
       if (d == 0) {
-        a.ws_m[row] = m;
+        a.ws_m[row] = Mx;
         a.ws_l[row] = l;
       }
     }

@@ -33,6 +33,19 @@ struct DecodeArgs {
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]
 };
 
+struct PrefillArgs {
+  KvCacheArgs cache;
+  void* out;
+  const void* query;
+  const int32_t* cu_q_lens;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t num_seqs, num_heads;
+  int32_t num_qtiles;  // query tiles per (sequence, KV head)
+  float scale;
+};
+
 constexpr int kMaxPartition = 1024;
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
@@ -43,5 +56,9 @@ hipError_t launch_reshape_and_cache(const KvCacheArgs& c, const void* key, const
                                     const int64_t* slots, int32_t num_tokens, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Query positions one prefill workgroup covers for a head group of `group`.
+int prefill_positions_per_tile(int group);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

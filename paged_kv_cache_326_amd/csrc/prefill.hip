@@ -1,0 +1,385 @@
+// Chunked-prefill attention over the paged cache on gfx950 matrix cores.
+//
+// Sources: [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践",
+// section "工程边界与架构取舍" (prefill is a compute-bound matrix product; a
+// long prompt is processed in chunks interleaved with decode steps) and
+// section "PagedAttention 的 CUDA Kernel 实现" (K/V reached block by block
+// through the table).
+//
+// A chunk of q_s new tokens of sequence s sits at positions ctx .. ctx+q_s-1
+// (ctx = seq_len - q_s; the chunk's own K/V are already in the pool) and
+// attends causally: position ctx+i sees keys 0 .. ctx+i.
+//
+// Work decomposition.  A workgroup (4 waves) owns 128 query rows that share
+// one KV head: the G heads of the group times 128/G consecutive positions.
+// Each wave owns 32 rows.  Keys stream through in tiles of 32: the tile's K
+// rows ([32][D]) and V rows, transposed to [D][32], are staged in LDS
+// (double-buffered: the next tile's global loads are in flight while the
+// current tile is used), then per wave
+//   S^T[32 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16 over D
+//   online softmax down each column (a column is one query row, held by a
+//   lane pair), P^T rounded to the storage type in registers
+//   O^T[D x 32 rows]     += V^T . P^T    v_mfma_f32_32x32x16 over the tile
+// Computing the transposed products keeps every operand a 16-byte LDS or
+// register read: the accumulator layout of S^T is directly the B operand of
+// the PV product once the S^T rows (keys) are permuted by swapping index bits
+// 2 and 3, and each lane's accumulators of O^T belong to one query row, so
+// the softmax rescale is a per-lane scalar.
+//
+// Operand layouts of v_mfma_f32_32x32x16 (lane l, e = 0..7, j = 0..15):
+//   A[m][k]: m = l % 32, k = 8 (l / 32) + e
+//   B[k][n]: k = 8 (l / 32) + e, n = l % 32
+//   C[m][n]: m = 8 (j / 4) + 4 (l / 32) + j % 4, n = l % 32
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_common.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPW = 4;     // waves per workgroup
+constexpr int kRows = 128; // query rows per workgroup
+constexpr int kKT = 32;    // keys per tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<bf16_t>(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<f16_t>(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two probabilities -> one packed pair of storage elements (round to nearest even).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+  const uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t to_bits(float x);
+template <>
+__device__ __forceinline__ uint16_t to_bits<bf16_t>(float x) {
+  return f32_to_bf16_bits(x);
+}
+template <>
+__device__ __forceinline__ uint16_t to_bits<f16_t>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int D>
+struct PrefillSmem {
+  static constexpr int kKStride = D + 8;     // K row stride (elements): 16-byte pad
+  static constexpr int kVStride = kKT + 8;   // V^T row stride (elements)
+  static constexpr int kKElems = kKT * kKStride;
+  static constexpr int kVElems = D * kVStride;
+  static constexpr int kBytes = 2 * (kKElems + kVElems) * 2;
+};
+
+template <typename T, int D, int B, int G>
+__global__ void __launch_bounds__(kPW * 64) prefill_kernel(PrefillArgs a) {
+  constexpr int QP = kRows / G;          // positions per workgroup
+  constexpr int KSTEPS = D / 16;         // QK contraction steps
+  constexpr int DT = D / 32;             // O^T row tiles
+  constexpr int NT = kPW * 64;
+  constexpr int CPT = kKT * D / 8 / NT;  // 16-byte chunks per thread per tile (K, and V)
+  using S = PrefillSmem<D>;
+  static_assert(CPT >= 1, "tile too small for the workgroup");
+
+  __shared__ __align__(16) uint16_t smem[S::kBytes / 2];
+  // Buffer b: K rows at smem + b*(K+V), V^T right after them.
+  auto Ks = [&](int b) { return smem + b * (S::kKElems + S::kVElems); };
+  auto Vt = [&](int b) { return smem + b * (S::kKElems + S::kVElems) + S::kKElems; };
+
+  // Work item.  Workgroup ids are dealt to the 8 XCDs round-robin; remap so
+  // that consecutive work items (the query tiles of one sequence and KV head,
+  // which read the same K/V) land on the same XCD and share its L2.
+  const int nqt = a.num_qtiles;
+  const int total = a.num_seqs * a.cache.num_kv_heads * nqt;
+  const int per_xcd = (total + 7) / 8;
+  const int u = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (u >= total) return;
+  const int qt = u % nqt;
+  const int g = (u / nqt) % a.cache.num_kv_heads;
+  const int s = u / nqt / a.cache.num_kv_heads;
+
+  const int qbeg = a.cu_q_lens[s];
+  const int q_len = a.cu_q_lens[s + 1] - qbeg;
+  const int q0 = qt * QP;
+  if (q0 >= q_len) return;
+  int L = a.seq_lens[s];
+  const int Lmax = a.max_blocks * B;
+  L = L > Lmax ? Lmax : L;
+  const int ctx = L - q_len;
+  if (ctx < 0) return;  // inconsistent lengths: nothing defined to compute
+  const int nvalid = min(QP, q_len - q0);
+  const int kend = ctx + q0 + nvalid;  // keys 0 .. kend-1 are visible to some row
+  const int ntiles = (kend + kKT - 1) / kKT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hi = lane >> 5;
+  const int Hkv = a.cache.num_kv_heads;
+  const int Hq = a.num_heads;
+
+  // This lane's query row (column n of the wave's S^T / O^T tiles).
+  const int r = w * 32 + n;
+  const int h = r / QP;
+  const int p = r % QP;
+  const bool row_ok = q0 + p < q_len;
+  const int limit = row_ok ? ctx + q0 + p : -1;
+  const int64_t tok = (int64_t)qbeg + q0 + p;
+  const int hq = g * G + h;
+
+  u32x4 qreg[KSTEPS];
+  {
+    const T* qrow = reinterpret_cast<const T*>(a.query) + (tok * Hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
+  }
+
+  const T* kc = reinterpret_cast<const T*>(a.cache.key_cache);
+  const T* vc = reinterpret_cast<const T*>(a.cache.value_cache);
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+
+  // Global -> registers for one tile.  K chunks: key-major (coalesced rows);
+  // V chunks: key-fastest, so the transposed LDS writes of a wave hit
+  // consecutive banks.  Keys beyond the sequence, or in blocks outside the
+  // pool, read as zeros (their probabilities are zero; a zero V keeps 0 * V
+  // finite).
+  u32x4 kreg[CPT], vreg[CPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      {
+        const int key = c / (D / 8), dch = c % (D / 8);
+        const int pos = t * kKT + key;
+        u32x4 x = {0, 0, 0, 0};
+        if (pos < L) {
+          const int pb = bt[pos / B];
+          if (pb >= 0 && pb < a.cache.num_blocks)
+            x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+        }
+        kreg[i] = x;
+      }
+      {
+        const int key = c % kKT, dch = c / kKT;
+        const int pos = t * kKT + key;
+        u32x4 x = {0, 0, 0, 0};
+        if (pos < L) {
+          const int pb = bt[pos / B];
+          if (pb >= 0 && pb < a.cache.num_blocks)
+            x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+        }
+        vreg[i] = x;
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      {
+        const int key = c / (D / 8), dch = c % (D / 8);
+        *reinterpret_cast<u32x4*>(Ks(buf) + key * S::kKStride + dch * 8) = kreg[i];
+      }
+      {
+        const int key = c % kKT, dch = c / kKT;
+        uint16_t* col = Vt(buf) + (dch * 8) * S::kVStride + key;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = vreg[i][e];
+          col[(2 * e) * S::kVStride] = (uint16_t)(wv & 0xffffu);
+          col[(2 * e + 1) * S::kVStride] = (uint16_t)(wv >> 16);
+        }
+      }
+    }
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float qscale = a.scale * kLog2e;
+  // S^T row slot of this lane's A operand, with bits 2 and 3 swapped.
+  const int krow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) fetch(t + 1);
+
+    // S^T = K . Q^T
+    f32x16 sacc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+    const uint16_t* krp = Ks(buf) + krow * S::kKStride + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      sacc = mfma32<T>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], sacc);
+
+    // Online softmax down the column.  Accumulator j holds key
+    // t*32 + 16 (j / 8) + 8 hi + j % 8 (after the row permutation).
+    const int kt0 = t * kKT + 8 * hi;
+    float z[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = kt0 + 16 * (j >> 3) + (j & 7);
+      z[j] = key <= limit ? sacc[j] * qscale : -INFINITY;
+      mt = fmaxf(mt, z[j]);
+    }
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    float alpha = 1.f;
+    float pj[16];
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pj[j] = 0.f;
+    } else {
+      alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pj[j] = z[j] == -INFINITY ? 0.f : fast_exp2(z[j] - m_new);
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ps += pj[j];
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+    }
+    // P^T as B operands.  f16 keeps 11 significant bits, enough on its own;
+    // bf16 keeps 8, so P is split into a bf16 head and a bf16 remainder and
+    // both are multiplied (the V^T operand is read once for the two).
+    u32x4 pb[2], pl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = pj[8 * ks + 2 * i], x1 = pj[8 * ks + 2 * i + 1];
+        pb[ks][i] = pack2<T>(x0, x1);
+        if constexpr (Elem<T>::kBytes == 2 && !std::is_same<T, f16_t>::value) {
+          const float h0 = __uint_as_float((pb[ks][i] & 0xffffu) << 16);
+          const float h1 = __uint_as_float(pb[ks][i] & 0xffff0000u);
+          pl[ks][i] = pack2<T>(x0 - h0, x1 - h1);
+        }
+      }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vrp = Vt(buf) + (32 * dt + n) * S::kVStride + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vrp + 16 * ks);
+        o[dt] = mfma32<T>(va, pb[ks], o[dt]);
+        if constexpr (!std::is_same<T, f16_t>::value) o[dt] = mfma32<T>(va, pl[ks], o[dt]);
+      }
+    }
+
+    if (t + 1 < ntiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Normalise and store this lane's row: accumulator j of tile dt is
+  // dimension 32 dt + 8 (j / 4) + 4 hi + j % 4.
+  const float l_tot = l_run + shfl_xor(l_run, 32);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (tok * Hq + hq) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d = 32 * dt + 8 * j4 + 4 * hi;
+        u32x2 pk;
+        pk[0] = (uint32_t)to_bits<T>(o[dt][4 * j4] * inv) | ((uint32_t)to_bits<T>(o[dt][4 * j4 + 1] * inv) << 16);
+        pk[1] = (uint32_t)to_bits<T>(o[dt][4 * j4 + 2] * inv) | ((uint32_t)to_bits<T>(o[dt][4 * j4 + 3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(orow + d) = pk;
+      }
+  }
+}
+
+template <typename T, int D, int B, int G>
+hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  const int total = a.num_seqs * a.cache.num_kv_heads * a.num_qtiles;
+  const int grid = ((total + 7) / 8) * 8;
+  hipLaunchKernelGGL((prefill_kernel<T, D, B, G>), dim3(grid), dim3(kPW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int B>
+hipError_t prefill_g(const PrefillArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_prefill_typed<T, D, B, 1>(a, stream);
+    case 2: return launch_prefill_typed<T, D, B, 2>(a, stream);
+    case 4: return launch_prefill_typed<T, D, B, 4>(a, stream);
+    case 8: return launch_prefill_typed<T, D, B, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+hipError_t prefill_b(const PrefillArgs& a, int G, hipStream_t stream) {
+  switch (a.cache.block_size) {
+    case 16: return prefill_g<T, D, 16>(a, G, stream);
+    case 32: return prefill_g<T, D, 32>(a, G, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t prefill_d(const PrefillArgs& a, int G, hipStream_t stream) {
+  switch (a.cache.head_dim) {
+    case 64: return prefill_b<T, 64>(a, G, stream);
+    case 128: return prefill_b<T, 128>(a, G, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int prefill_positions_per_tile(int group) { return kRows / group; }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.num_qtiles == 0) return hipSuccess;
+  const int G = a.num_heads / a.cache.num_kv_heads;
+  switch (a.cache.dtype) {
+    case DType::kF16: return prefill_d<f16_t>(a, G, stream);
+    case DType::kBF16: return prefill_d<bf16_t>(a, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -49,6 +49,7 @@ EXPORTS = (
     "pa_decode_workspace_bytes",
     "pa_decode",
     "pa_decode_ex",
+    "pa_prefill_chunk",
     "pa_status_string",
     "pa_version",
 )
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_ex.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp]
     L.pa_decode_ex.restype = ctypes.c_int
+    L.pa_prefill_chunk.argtypes = [cache_p, vp, vp, i32p, i32p, i32p, i32, i32, i32, i32, f32, vp]
+    L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -178,6 +181,25 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale:
                             seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(), ws_bytes,
                             int(partition_size), _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, block_tables, scale: float,
+                     max_q_len: int, stream=None):
+    c = kv_cache(key_cache, value_cache)
+    _need(query, "query", key_cache.dtype)
+    _need(out, "out", key_cache.dtype)
+    _need(cu_q_lens, "cu_q_lens", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_tables, "block_tables", torch.int32)
+    S = seq_lens.shape[0]
+    T, Hq, D = query.shape
+    if out.shape != query.shape or D != c.head_dim or cu_q_lens.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between query/out/cu_q_lens/seq_lens/block_tables and the cache")
+    st = lib().pa_prefill_chunk(ctypes.byref(c), out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), seq_lens.data_ptr(),
+                                block_tables.data_ptr(), block_tables.shape[1], S, Hq, int(max_q_len), float(scale),
+                                _stream(stream))
+    _check(st, "pa_prefill_chunk")
     return out
 
 

@@ -104,6 +104,19 @@ class GpuWorkload:
                      self.w.scale, self.w.max_seq_len, workspace=workspace, partition_size=partition_size)
         return self.out
 
+    def prefill(self, max_q_len=None):
+        from paged_kv_cache_326_amd import pa
+
+        mq = int(self.w.q_lens.max()) if max_q_len is None else max_q_len
+        pa.pa_prefill_chunk(self.out, self.query, self.key_cache, self.value_cache, self.cu_q_lens, self.seq_lens,
+                            self.block_tables, self.w.scale, mq)
+        return self.out
+
+    def share_pool(self, other: "GpuWorkload"):
+        """Use another workload's (already scattered) pool."""
+        self.key_cache, self.value_cache = other.key_cache, other.value_cache
+        return self
+
     def step(self, partition_size=0):
         """slot mapping -> scatter -> decode, all on the current stream."""
         self.slots()
@@ -129,6 +142,15 @@ def oracle_step(w: synth.Workload, seqs=None):
     q = oracle.to_float64(w.query, dt)
     out = oracle.decode_attention(q[idx], kc, vc, w.block_tables[idx], w.seq_lens[idx], w.scale)
     return slots, kc, vc, out
+
+
+def oracle_prefill(w: synth.Workload, kc, vc):
+    """Oracle chunked-prefill output for every sequence of `w` over scattered
+    float64 caches."""
+    import oracle
+
+    q = oracle.to_float64(w.query, w.dtype)
+    return oracle.prefill_attention(q, w.cu_q_lens, kc, vc, w.block_tables, w.seq_lens, w.scale)
 
 
 def oracle_scatter_storage(w: synth.Workload):
