@@ -2,8 +2,8 @@
 """Paged-decode benchmark on one MI355X.
 
 One step is the whole hot path over one batch: slot mapping of the new
-tokens, the KV scatter into the pool, then decode attention over every
-sequence's paged K/V (partition kernel + merge).  The default workload is one
+tokens and their KV scatter into the pool (one fused launch), then decode
+attention over every sequence's paged K/V (partition kernel + merge).  The default workload is one
 LLaMA-2-70B-shaped layer: 16 sequences x 4096 tokens, 64 query / 8 KV heads,
 head_dim 128, fp16, block size 16, a randomly permuted pool of 4096 blocks.
 
@@ -139,8 +139,7 @@ def main():
 
     def step(i, ev=None):
         c = copies[i % len(copies)]
-        c.slots()
-        c.scatter()
+        c.append()  # slot mapping + KV scatter of the new tokens, one launch
         if ev is not None:
             ev[0].record(stream)
         c.decode(partition_size=P, workspace=ws[i % len(copies)])

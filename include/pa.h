@@ -116,6 +116,20 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const 
                                const int64_t* slot_mapping, int32_t num_tokens,
                                hipStream_t stream);
 
+/* pa_slot_mapping and pa_reshape_and_cache in one launch: computes every new
+ * token's slot from the block table (same definition and -1 rule as
+ * pa_slot_mapping), stores it to slot_mapping, and copies the token's K and V
+ * there; tokens whose slot is -1 or whose physical block lies outside the
+ * pool are not written.  Arguments as in the two calls; max_q_len is a
+ * host-side upper bound of the per-sequence new-token counts and num_tokens
+ * = cu_q_lens[num_seqs].
+ */
+pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* value,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t num_seqs,
+                       int32_t max_q_len, int64_t* slot_mapping, int32_t num_tokens,
+                       hipStream_t stream);
+
 /* Partition length (tokens) that pa_decode picks when partition_size is 0. */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                                  int32_t block_size);

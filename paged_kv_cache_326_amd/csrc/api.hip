@@ -96,6 +96,20 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const 
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* value, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* cu_q_lens,
+                       int32_t num_seqs, int32_t max_q_len, int64_t* slot_mapping, int32_t num_tokens,
+                       hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (!key || !value || !block_tables || !seq_lens || !cu_q_lens || !slot_mapping) return PA_ERR_NULL;
+  const hipError_t e = pa::launch_append(to_args(cache), key, value, block_tables, max_blocks_per_seq, seq_lens,
+                                         cu_q_lens, num_seqs, max_q_len, slot_mapping, num_tokens, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {
   // Aim for at least four workgroups per compute unit; longer partitions
   // amortise the merge, shorter ones fill the chip when there are few

@@ -65,6 +65,83 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+// Slot mapping and scatter in one pass.  Workgroup (x, s) covers new tokens
+// x*kAppendTok .. of sequence s; thread (token, chunk) fetches its 16-byte
+// K or V chunk (independent of the slot, so the load overlaps the table
+// lookup), computes the slot and stores.  The chunk-0 thread of each token
+// also records the slot.
+constexpr int kAppendTok = 8;
+
+template <typename T>
+__global__ void __launch_bounds__(256) append_kernel(
+    T* __restrict__ key_cache, T* __restrict__ value_cache, const T* __restrict__ key,
+    const T* __restrict__ value, const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q_lens, int64_t* __restrict__ slots,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks) {
+  constexpr int VEC = vec16<T>();
+  const int s = blockIdx.y;
+  const int t0 = cu_q_lens[s];
+  const int q = cu_q_lens[s + 1] - t0;
+  const int L = seq_lens[s];
+  const int chunks_per_row = head_dim / VEC;
+  const int chunks_per_tok = num_kv_heads * chunks_per_row * 2;  // K and V
+  const int first = blockIdx.x * kAppendTok;
+  for (int idx = threadIdx.x; idx < kAppendTok * chunks_per_tok; idx += blockDim.x) {
+    const int i = first + idx / chunks_per_tok;
+    if (i >= q) break;
+    const int t = t0 + i;
+    if (t < 0 || t >= num_tokens) continue;
+    const int c = idx % chunks_per_tok;
+    const int which = c / (num_kv_heads * chunks_per_row);
+    const int h = (c / chunks_per_row) % num_kv_heads;
+    const int ch = c % chunks_per_row;
+    const T* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
+    const u32x4 data = *reinterpret_cast<const u32x4*>(src);
+    const int pos = L - q + i;
+    int64_t slot = -1, phys = -1;
+    if (pos >= 0 && pos / block_size < max_blocks) {
+      phys = block_tables[(int64_t)s * max_blocks + pos / block_size];
+      slot = phys * block_size + pos % block_size;
+    }
+    if (c == 0) slots[t] = slot;
+    if (slot < 0 || phys >= num_blocks) continue;
+    const int64_t blk = slot / block_size;
+    const int off = (int)(slot % block_size);
+    T* dst = (which ? value_cache : key_cache) + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
+    *reinterpret_cast<u32x4*>(dst) = data;
+  }
+}
+
+template <typename T>
+static hipError_t launch_append_t(const KvCacheArgs& c, const void* key, const void* value,
+                                  const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                                  const int32_t* cu_q_lens, int32_t num_seqs, int32_t max_q_len, int64_t* slots,
+                                  int32_t num_tokens, hipStream_t stream) {
+  if (num_seqs == 0 || max_q_len == 0) return hipSuccess;
+  dim3 grid((max_q_len + kAppendTok - 1) / kAppendTok, num_seqs);
+  hipLaunchKernelGGL(append_kernel<T>, grid, dim3(256), 0, stream, (T*)c.key_cache, (T*)c.value_cache, (const T*)key,
+                     (const T*)value, block_tables, max_blocks, seq_lens, cu_q_lens, slots, num_tokens, c.num_kv_heads,
+                     c.head_dim, c.block_size, c.num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* value, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t num_seqs,
+                         int32_t max_q_len, int64_t* slots, int32_t num_tokens, hipStream_t stream) {
+  switch (c.dtype) {
+    case DType::kF32:
+      return launch_append_t<float>(c, key, value, block_tables, max_blocks, seq_lens, cu_q_lens, num_seqs, max_q_len,
+                                    slots, num_tokens, stream);
+    case DType::kF16:
+      return launch_append_t<f16_t>(c, key, value, block_tables, max_blocks, seq_lens, cu_q_lens, num_seqs, max_q_len,
+                                    slots, num_tokens, stream);
+    case DType::kBF16:
+      return launch_append_t<bf16_t>(c, key, value, block_tables, max_blocks, seq_lens, cu_q_lens, num_seqs,
+                                     max_q_len, slots, num_tokens, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                                const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
                                int64_t* slots, int32_t num_tokens, hipStream_t stream) {

@@ -194,6 +194,47 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Combine the per-partition partials of one (sequence, query head, dim):
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Partials are fetched in batches of kMergeBatch, every load of a batch
+// issued before any is used; batches combine with a running rescale.
+constexpr int kMergeBatch = 16;
+
+template <typename T, int D>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
+  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const bool ok = p0 + i < np;
+      const int64_t row = row0 + p0 + i;
+      mv[i] = ok ? a.ws_m[row] : -INFINITY;
+      lv[i] = ok ? a.ws_l[row] : 0.f;
+      ov[i] = ok ? a.ws_o[row * D + d] : 0.f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, mv[i]);
+    if (Mb == -INFINITY) continue;
+    if (M != -INFINITY) {
+      const float f = fast_exp2(M - Mb);
+      num *= f;
+      den *= f;
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const float wgt = mv[i] == -INFINITY ? 0.f : fast_exp2(mv[i] - Mb);
+      num = fmaf(wgt, ov[i], num);
+      den = fmaf(wgt, lv[i], den);
+    }
+    M = Mb;
+  }
+  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d;
+  store_elem<T>(out, den > 0.f ? num / den : 0.f);
+}
+
 template <typename T, int G>
 struct Occupancy {
   // 2-byte types fit in 128 VGPRs (4 waves per SIMD); f32 is a correctness
@@ -520,30 +561,17 @@ decode_partition_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the partitions of sequences longer than one partition.
+// Merge kernel for sequences longer than one partition.  A fused variant
+// (the last workgroup of a sequence and KV head merging after an agent-scope
+// release/acquire on an arrival counter) is correct but on gfx950 every such
+// release writes back the XCD's L2, which cost far more than this launch.
 // grid (num_heads, num_seqs), D threads.
 template <typename T, int D>
 __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x;
-  const int s = blockIdx.y;
-  const int d = threadIdx.x;
-  int L = a.seq_lens[s];
+  int L = a.seq_lens[blockIdx.y];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   if (L <= a.partition) return;  // written directly by the partition kernel
-  const int np = (L + a.partition - 1) / a.partition;
-  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[row0 + p]);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p < np; ++p) {
-      const float wgt = fast_exp2(a.ws_m[row0 + p] - M);
-      num = fmaf(wgt, a.ws_o[(row0 + p) * D + d], num);
-      den = fmaf(wgt, a.ws_l[row0 + p], den);
-    }
-  }
-  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d;
-  store_elem<T>(out, den > 0.f ? num / den : 0.f);
+  merge_partials<T, D>(a, blockIdx.y, blockIdx.x, threadIdx.x, (L + a.partition - 1) / a.partition);
 }
 
 template <typename T, int D, int B, int G>

@@ -55,6 +55,10 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, 
 hipError_t launch_reshape_and_cache(const KvCacheArgs& c, const void* key, const void* value,
                                     const int64_t* slots, int32_t num_tokens, hipStream_t stream);
 
+hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* value, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t num_seqs,
+                         int32_t max_q_len, int64_t* slots, int32_t num_tokens, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Query positions one prefill workgroup covers for a head group of `group`.

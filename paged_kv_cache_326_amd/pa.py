@@ -45,6 +45,7 @@ _lib = None
 EXPORTS = (
     "pa_slot_mapping",
     "pa_reshape_and_cache",
+    "pa_append_kv",
     "pa_decode_auto_partition",
     "pa_decode_workspace_bytes",
     "pa_decode",
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.pa_slot_mapping.restype = ctypes.c_int
     L.pa_reshape_and_cache.argtypes = [cache_p, vp, vp, i64p, i32, vp]
     L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_append_kv.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32p, i32, i32, i64p, i32, vp]
+    L.pa_append_kv.restype = ctypes.c_int
     L.pa_decode_auto_partition.argtypes = [i32, i32, i32, i32]
     L.pa_decode_auto_partition.restype = i32
     L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -146,6 +149,28 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, strea
         raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] with one slot per token")
     st = lib().pa_reshape_and_cache(ctypes.byref(c), key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), T, _stream(stream))
     _check(st, "pa_reshape_and_cache")
+
+
+def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len: int,
+                 slot_mapping=None, stream=None):
+    c = kv_cache(key_cache, value_cache)
+    _need(key, "key", key_cache.dtype)
+    _need(value, "value", key_cache.dtype)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(cu_q_lens, "cu_q_lens", torch.int32)
+    T = key.shape[0]
+    S = seq_lens.shape[0]
+    if key.shape != (T, c.num_kv_heads, c.head_dim) or value.shape != key.shape or cu_q_lens.shape[0] != S + 1:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim]; cu_q_lens [num_seqs + 1]")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(T, dtype=torch.int64, device=key.device)
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    st = lib().pa_append_kv(ctypes.byref(c), key.data_ptr(), value.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+                            seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, int(max_q_len), slot_mapping.data_ptr(), T,
+                            _stream(stream))
+    _check(st, "pa_append_kv")
+    return slot_mapping
 
 
 def pa_decode_auto_partition(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int) -> int:

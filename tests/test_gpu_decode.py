@@ -57,6 +57,20 @@ def test_slot_mapping_and_scatter_bitexact(k):
         assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_append_kv_bitexact(k):
+    # Slot mapping + scatter fused in one launch: same slots, same pool bytes.
+    w = synth.config(k)
+    gw = harness.GpuWorkload(w)
+    slots = gw.append()
+    _sync()
+    ref_slots, ref_kc, ref_vc = harness.oracle_scatter_storage(w)
+    np.testing.assert_array_equal(slots.cpu().numpy(), ref_slots)
+    for got, ref in ((gw.key_cache, ref_kc), (gw.value_cache, ref_vc)):
+        g = harness.from_device(got, w.dtype)
+        assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
+
+
 def test_scatter_skips_negative_slots():
     import torch
 
