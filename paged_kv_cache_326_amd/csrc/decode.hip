@@ -128,10 +128,15 @@ __device__ __forceinline__ float reduce_scatter8(float* a, int sub) {
   return a[0];
 }
 
-// LDS layout of one workgroup.  Each wave owns a logit/probability region
-// and a slot for its partial output; the block-table slice is shared.
+// LDS layout of one workgroup.  Each wave owns one region that first holds
+// its logits/probabilities and, once its PV pass is done, its partial output
+// (only the owning wave ever touches its region, so the reuse needs no
+// barrier); f16 probability pairs, the per-wave (m, l), the block-table
+// slice and the query rows are separate.  At the benchmark shape the total
+// is ~27 KiB, so LDS never limits the four workgroups per CU that the VGPR
+// budget allows.
 struct SmemLayout {
-  int bt_off, p_off, p_wave, h_off, h_wave, o_off, m_off, l_off, bytes;
+  int bt_off, p_off, p_wave, h_off, h_wave, m_off, l_off, q_off, bytes;
 };
 
 __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, int D) {
@@ -142,17 +147,18 @@ __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, i
   s.bt_off = off;
   off += (nblk * 4 + 15) & ~15;
   s.p_off = off;
-  s.p_wave = bpw * B * G;  // floats per wave
+  const int logits = bpw * B * G;  // floats
+  s.p_wave = logits > G * D ? logits : G * D;
   off += kNW * s.p_wave * 4;
   s.h_off = off;
   s.h_wave = bpw * B / 2 * G;  // dwords per wave: f16 probability pairs
   off += kNW * s.h_wave * 4;
-  s.o_off = off;
-  off += kNW * G * D * 4;
   s.m_off = off;
   off += kNW * G * 4;
   s.l_off = off;
   off += kNW * G * 4;
+  s.q_off = off;  // the G query rows, as stored (at most 8 x 128 x 4 bytes)
+  off += G * D * 4;
   s.bytes = off;
   return s;
 }
@@ -196,13 +202,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Combine the per-partition partials of one (sequence, query head, dim):
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// Partials are fetched in batches of kMergeBatch, every load of a batch
-// issued before any is used; batches combine with a running rescale.
+// Every one of the call's partitions is fetched (empty ones carry
+// m = -inf and contribute nothing), in batches of kMergeBatch whose loads are
+// all issued before any is used; batches combine with a running rescale.
 constexpr int kMergeBatch = 16;
 
-template <typename T, int D>
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
-  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
+template <int D>
+__device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d) {
+  const int np = a.num_partitions;
+  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * np;
   float M = -INFINITY, num = 0.f, den = 0.f;
   for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
@@ -225,14 +233,15 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
     }
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const float wgt = mv[i] == -INFINITY ? 0.f : fast_exp2(mv[i] - Mb);
-      num = fmaf(wgt, ov[i], num);
-      den = fmaf(wgt, lv[i], den);
+      // Absent partitions are skipped by select: their l and o are stale.
+      const bool live = mv[i] != -INFINITY;
+      const float wgt = live ? fast_exp2(mv[i] - Mb) : 0.f;
+      num = live ? fmaf(wgt, ov[i], num) : num;
+      den = live ? fmaf(wgt, lv[i], den) : den;
     }
     M = Mb;
   }
-  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d;
-  store_elem<T>(out, den > 0.f ? num / den : 0.f);
+  return den > 0.f ? num / den : 0.f;
 }
 
 template <typename T, int G>
@@ -269,19 +278,31 @@ decode_partition_kernel(DecodeArgs a) {
   const int P = a.partition;
   const SmemLayout lay = smem_layout(P, B, G, D);
 
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int tok0 = part * P;
-  if (part > 0 && tok0 >= L) return;
-  const int ntok = min(P, L - tok0) > 0 ? min(P, L - tok0) : 0;
-  const int nblk = (ntok + B - 1) / B;
-  const bool direct = L <= P;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int Hkv = a.cache.num_kv_heads;
   const int Hq = a.num_heads;
+  const int tok0 = part * P;
+  const int blk0 = tok0 / B;
+
+  // The table slice of the whole partition range is fetched without waiting
+  // for seq_len (it lies inside the table row either way), so the two loads
+  // overlap; entries past the sequence's end are never used.
+  int bt_id = -1;
+  if (tid < P / B && blk0 + tid < a.max_blocks) bt_id = a.block_tables[(int64_t)s * a.max_blocks + blk0 + tid];
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const bool direct = L <= P;
+  if (part > 0 && tok0 >= L) {
+    // An empty partition of a split sequence marks its partials as absent
+    // (m = -inf) so the merge can fetch every partition unconditionally.
+    if (!direct && tid < G) a.ws_m[((int64_t)s * Hq + g * G + tid) * a.num_partitions + part] = -INFINITY;
+    return;
+  }
+  const int ntok = min(P, L - tok0) > 0 ? min(P, L - tok0) : 0;
+  const int nblk = (ntok + B - 1) / B;
+
   int* s_bt = reinterpret_cast<int*>(smem + lay.bt_off);
   float* s_p = reinterpret_cast<float*>(smem + lay.p_off) + w * lay.p_wave;
   // f16 path: probabilities of token pairs (t, t + TS) packed as f16x2, one
@@ -289,35 +310,36 @@ decode_partition_kernel(DecodeArgs a) {
   // loaded by PV load i of chunk jc in slot ts.
   uint32_t* s_h = reinterpret_cast<uint32_t*>(smem + lay.h_off) + w * lay.h_wave;
   constexpr bool kDot2PV = std::is_same<T, f16_t>::value;
-  float* s_o = reinterpret_cast<float*>(smem + lay.o_off);
+  // Wave w's partial output, once its PV pass is done: [G][D] floats at the
+  // start of region w.
+  float* s_o = reinterpret_cast<float*>(smem + lay.p_off);
   float* s_m = reinterpret_cast<float*>(smem + lay.m_off);
   float* s_l = reinterpret_cast<float*>(smem + lay.l_off);
 
   // 1. Block-table slice -> LDS.  Entries outside the pool become -1.
+  if (tid < P / B) s_bt[tid] = (bt_id < 0 || bt_id >= a.cache.num_blocks) ? -1 : bt_id;
+
+  // The G query rows of this KV head are fetched once per workgroup into LDS
+  // (G*D elements, 16 bytes per thread); every lane then reads its slices
+  // from there, eight lanes per address.
+  T* s_q = reinterpret_cast<T*>(smem + lay.q_off);
   {
-    const int blk0 = tok0 / B;
-    for (int j = tid; j < nblk; j += NT) {
-      const int lj = blk0 + j;
-      int id = lj < a.max_blocks ? a.block_tables[(int64_t)s * a.max_blocks + lj] : -1;
-      if (id < 0 || id >= a.cache.num_blocks) id = -1;
-      s_bt[j] = id;
-    }
+    const T* qb = reinterpret_cast<const T*>(a.query) + ((int64_t)s * Hq + g * G) * D;
+    for (int c = tid; c < G * D / VEC; c += NT)
+      *reinterpret_cast<u32x4*>(s_q + c * VEC) = *reinterpret_cast<const u32x4*>(qb + c * VEC);
   }
+  __syncthreads();
 
   // Query slices for the QK layout: lane `sub` of a token holds, for each
   // head, dims c*LPT*VEC + sub*VEC .. +VEC of every chunk c.
   const int sub = lane & (LPT - 1);
   const int tq = lane / LPT;
   u32x4 qv[G][NCK];
-  {
-    const T* qb = reinterpret_cast<const T*>(a.query) + ((int64_t)s * Hq + g * G) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int c = 0; c < NCK; ++c)
-        qv[h][c] = *reinterpret_cast<const u32x4*>(qb + h * D + c * LPT * VEC + sub * VEC);
-  }
-  __syncthreads();
+    for (int c = 0; c < NCK; ++c)
+      qv[h][c] = *reinterpret_cast<const u32x4*>(s_q + h * D + c * LPT * VEC + sub * VEC);
 
   // This wave's blocks: local index jl -> partition block w + jl*NW.
   const int nbw = nblk > w ? (nblk - w + kNW - 1) / kNW : 0;
@@ -510,6 +532,7 @@ decode_partition_kernel(DecodeArgs a) {
 
   // 5. Fold token slots, park the wave's partial in LDS, merge the waves.
   reduce_slots<NV, TS>(o);
+  wave_lds_sync();  // this wave's probability reads are done before its region is reused
   {
     constexpr int R = TS < 4 ? TS : 4;
     constexpr int PER = NV / R;  // values per lane after the fold
@@ -520,7 +543,7 @@ decode_partition_kernel(DecodeArgs a) {
       for (int j = 0; j < PER; ++j) {
         const int k = q * PER + j;
         const int h = k / VEC, v = k % VEC;
-        s_o[(w * G + h) * D + col * VEC + v] = o[j];
+        s_o[w * lay.p_wave + h * D + col * VEC + v] = o[j];
       }
     }
   }
@@ -542,7 +565,7 @@ decode_partition_kernel(DecodeArgs a) {
       for (int ww = 0; ww < kNW; ++ww) {
         const float mw = s_m[ww * G + h];
         const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - Mx);
-        acc = fmaf(sc, s_o[(ww * G + h) * D + d], acc);
+        acc = fmaf(sc, s_o[ww * lay.p_wave + h * D + d], acc);
         l = fmaf(sc, s_l[ww * G + h], l);
       }
     }
@@ -568,10 +591,12 @@ decode_partition_kernel(DecodeArgs a) {
 // grid (num_heads, num_seqs), D threads.
 template <typename T, int D>
 __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
-  int L = a.seq_lens[blockIdx.y];
+  const int s = blockIdx.y, hq = blockIdx.x, d = threadIdx.x;
+  int L = a.seq_lens[s];  // independent of the partial loads below
+  const float v = merge_partials<D>(a, s, hq, d);
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   if (L <= a.partition) return;  // written directly by the partition kernel
-  merge_partials<T, D>(a, blockIdx.y, blockIdx.x, threadIdx.x, (L + a.partition - 1) / a.partition);
+  store_elem<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
 }
 
 template <typename T, int D, int B, int G>
