@@ -34,6 +34,25 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_llama2-70b-bs16x4096_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_326_amd", "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter record, or None
+    when the decode kernel source has changed since the counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_sha256") != src:
+        return None
+    return int(rec["bytes_per_call"])
+
+
 def algorithmic_decode_bytes(w) -> int:
     """K+V of every attended token, query in, output out, the block-table
     entries actually read, and seq_lens."""
@@ -43,6 +62,105 @@ def algorithmic_decode_bytes(w) -> int:
     qo = 2 * w.num_seqs * w.num_heads * w.head_dim * dt
     bt = int(sum(-(-int(L) // B) for L in w.seq_lens)) * 4
     return kv + qo + bt + 4 * w.num_seqs
+
+
+def prefill_flops(w) -> int:
+    """4*D flops per causally visible (query, key) pair per query head."""
+    pairs = 0
+    for L, q in zip(w.seq_lens.tolist(), w.q_lens.tolist()):
+        ctx = L - q
+        pairs += q * ctx + q * (q + 1) // 2
+    return 4 * w.head_dim * w.num_heads * pairs
+
+
+def _median_us(fn, iters=50, warm=5):
+    import torch
+
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def _copies(w, n):
+    import torch
+    from tests import harness
+
+    first = harness.GpuWorkload(w)
+    out = [first]
+    for _ in range(n - 1):
+        g = harness.GpuWorkload.__new__(harness.GpuWorkload)
+        g.__dict__.update({k: (v.clone() if torch.is_tensor(v) else v) for k, v in first.__dict__.items()})
+        out.append(g)
+    for c in out:
+        c.append()
+    return out
+
+
+def secondary(copies_n: int):
+    """Decode on the other decode configs, chunked prefill on the mixed config,
+    and the benchmark layer with an unpermuted (identity) block layout."""
+    import torch
+    from paged_kv_cache_326_amd import pa, synth
+
+    res = {}
+    for k in (3, 4):
+        w = synth.config(k, poison_unused=False)
+        cs = _copies(w, copies_n)
+        ws = [pa.decode_workspace(c.query, c.key_cache, w.max_seq_len) for c in cs]
+        t = _median_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
+        nb = algorithmic_decode_bytes(w)
+        uniq = int((w.refcounts > 0).sum()) * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes * 2
+        res[synth.CONFIG_NAMES[k]] = {
+            "decode_us": round(t, 2), "algorithmic_bytes": nb, "GBps": round(nb / t / 1e3, 1),
+            "frac_of_hbm_peak": round(nb / t / 1e3 / HBM_PEAK_GBS, 4),
+            "attended_tokens_per_s": int(w.seq_lens.sum()) / (t * 1e-6),
+            "unique_kv_bytes": uniq, "dtype": w.dtype,
+        }
+        del cs, ws
+        torch.cuda.empty_cache()
+    # Mixed chunked prefill + decode.
+    w = synth.config(5, poison_unused=False)
+    pre, dec = synth.prefill_decode_split(w)
+    cs = _copies(w, copies_n)
+    wp, wd = w.subset(pre), w.subset(dec)
+    from tests import harness
+
+    gps = [harness.GpuWorkload(wp).share_pool(c) for c in cs]
+    gds = [harness.GpuWorkload(wd).share_pool(c) for c in cs]
+    wsd = [pa.decode_workspace(g.query, g.key_cache, wd.max_seq_len) for g in gds]
+    tp = _median_us(lambda i: gps[i % len(gps)].prefill(), iters=20)
+    td = _median_us(lambda i: gds[i % len(gds)].decode(workspace=wsd[i % len(gds)]))
+    fl = prefill_flops(wp)
+    nbd = algorithmic_decode_bytes(wd)
+    res[synth.CONFIG_NAMES[5]] = {
+        "prefill_us": round(tp, 2), "prefill_flops": fl, "prefill_TFLOPs": round(fl / tp / 1e6, 1),
+        "prefill_frac_of_mfma_peak": round(fl / tp / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_us": round(td, 2), "decode_GBps": round(nbd / td / 1e3, 1),
+        "decode_frac_of_hbm_peak": round(nbd / td / 1e3 / HBM_PEAK_GBS, 4), "dtype": w.dtype,
+    }
+    del cs, gps, gds, wsd
+    torch.cuda.empty_cache()
+    # Indirection: identity vs permuted layout of the benchmark layer.
+    w = synth.config(2, poison_unused=False)
+    out = {}
+    for name, ww in (("permuted", w), ("identity", synth.identity_tables(w))):
+        cs = _copies(ww, copies_n)
+        ws = [pa.decode_workspace(c.query, c.key_cache, ww.max_seq_len) for c in cs]
+        out[name] = _median_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
+        del cs, ws
+        torch.cuda.empty_cache()
+    res["block_table_indirection"] = {
+        "permuted_us": round(out["permuted"], 2), "identity_us": round(out["identity"], 2),
+        "overhead_pct": round(100.0 * (out["permuted"] / out["identity"] - 1.0), 2),
+    }
+    return res
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -92,6 +210,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="rotated pool copies")
     ap.add_argument("--identity-tables", action="store_true", help="unpermuted block layout (indirection overhead)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -201,7 +320,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic() if args.config == 2 and not args.identity_tables else None,
             "algorithmic_bytes": nbytes,
             "decode_us_mean": float(dec_ms.mean()) * 1e3,
             "decode_us_median": float(np.median(dec_ms)) * 1e3,
@@ -210,6 +329,10 @@ def main():
         },
         "attended_kv_tokens_per_s_decode": attended / dec_avg_s,
     }
+    if not args.no_secondary and args.config == 2 and not args.identity_tables:
+        del copies, ws
+        torch.cuda.empty_cache()
+        rec["secondary"] = secondary(args.copies)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -272,9 +272,15 @@ decode_partition_kernel(DecodeArgs a) {
   static_assert(64 % G == 0, "group size must divide the wave");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  // 1-D grid, (sequence, KV head) fastest and partition slowest.  Workgroup
+  // ids are dealt to the 8 XCDs round-robin, so this hands each XCD whole
+  // (sequence, KV head) pairs; with the partition fastest, XCD x would get
+  // partitions x and x+8 of everything and every short sequence's only
+  // partition would pile onto XCD 0.
+  const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
+  const int part = blockIdx.x / (a.num_seqs * a.cache.num_kv_heads);
+  const int g = sg % a.cache.num_kv_heads;
+  const int s = sg / a.cache.num_kv_heads;
   const int P = a.partition;
   const SmemLayout lay = smem_layout(P, B, G, D);
 
@@ -602,7 +608,7 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
 template <typename T, int D, int B, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const SmemLayout lay = smem_layout(a.partition, B, G, D);
-  dim3 grid(a.num_partitions > 0 ? a.num_partitions : 1, a.cache.num_kv_heads, a.num_seqs);
+  dim3 grid((unsigned)((a.num_partitions > 0 ? a.num_partitions : 1) * a.cache.num_kv_heads * a.num_seqs));
   hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G>), grid, dim3(kNW * 64), lay.bytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
