@@ -44,6 +44,7 @@ namespace {
 constexpr int kPW = 4;     // waves per workgroup
 constexpr int kRows = 128; // query rows per workgroup
 constexpr int kKT = 32;    // keys per tile
+constexpr int kBtStage = 2048;  // table entries staged in LDS (32K tokens at block size 16)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -95,7 +96,7 @@ struct PrefillSmem {
 };
 
 template <typename T, int D, int B, int G>
-__global__ void __launch_bounds__(kPW * 64) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2))) prefill_kernel(PrefillArgs a) {
   constexpr int QP = kRows / G;          // positions per workgroup
   constexpr int KSTEPS = D / 16;         // QK contraction steps
   constexpr int DT = D / 32;             // O^T row tiles
@@ -162,12 +163,34 @@ __global__ void __launch_bounds__(kPW * 64) prefill_kernel(PrefillArgs a) {
   const T* kc = reinterpret_cast<const T*>(a.cache.key_cache);
   const T* vc = reinterpret_cast<const T*>(a.cache.value_cache);
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+  // The table entries this workgroup needs are staged in LDS once (the tile
+  // loop would otherwise pay a dependent global read before every K/V load);
+  // tables longer than the staging area are read from global memory.
+  __shared__ int s_bt[kBtStage];
+  const int nbk = (kend + B - 1) / B;
+  const bool staged = nbk <= kBtStage;
+  if (staged) {
+    for (int j = tid; j < nbk; j += NT) {
+      const int id = bt[j];
+      s_bt[j] = (id >= 0 && id < a.cache.num_blocks) ? id : -1;
+    }
+  }
+  __syncthreads();
+  // Callers pass pos < kend, so pos / B < nbk; the bound is checked anyway
+  // so that no index outside the staged (validated) entries is ever used.
+  auto block_of = [&](int pos) -> int {
+    const int j = pos / B;
+    if (j >= nbk) return -1;
+    if (staged) return s_bt[j];
+    const int id = bt[j];
+    return (id >= 0 && id < a.cache.num_blocks) ? id : -1;
+  };
 
   // Global -> registers for one tile.  K chunks: key-major (coalesced rows);
   // V chunks: key-fastest, so the transposed LDS writes of a wave hit
-  // consecutive banks.  Keys beyond the sequence, or in blocks outside the
-  // pool, read as zeros (their probabilities are zero; a zero V keeps 0 * V
-  // finite).
+  // consecutive banks.  Keys no row of this workgroup sees (>= kend), or in
+  // blocks outside the pool, read as zeros (their probabilities are zero; a
+  // zero V keeps 0 * V finite).
   u32x4 kreg[CPT], vreg[CPT];
   auto fetch = [&](int t) {
 #pragma unroll
@@ -177,10 +200,9 @@ __global__ void __launch_bounds__(kPW * 64) prefill_kernel(PrefillArgs a) {
         const int key = c / (D / 8), dch = c % (D / 8);
         const int pos = t * kKT + key;
         u32x4 x = {0, 0, 0, 0};
-        if (pos < L) {
-          const int pb = bt[pos / B];
-          if (pb >= 0 && pb < a.cache.num_blocks)
-            x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+        if (pos < kend) {  // keys >= kend are masked for every row of this tile
+          const int pb = block_of(pos);
+          if (pb >= 0) x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
         }
         kreg[i] = x;
       }
@@ -188,10 +210,9 @@ __global__ void __launch_bounds__(kPW * 64) prefill_kernel(PrefillArgs a) {
         const int key = c % kKT, dch = c / kKT;
         const int pos = t * kKT + key;
         u32x4 x = {0, 0, 0, 0};
-        if (pos < L) {
-          const int pb = bt[pos / B];
-          if (pb >= 0 && pb < a.cache.num_blocks)
-            x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+        if (pos < kend) {  // keys >= kend are masked for every row of this tile
+          const int pb = block_of(pos);
+          if (pb >= 0) x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
         }
         vreg[i] = x;
       }
