@@ -111,13 +111,13 @@ pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* va
 }
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {
-  // Aim for at least four workgroups per compute unit; longer partitions
-  // amortise the merge, shorter ones fill the chip when there are few
-  // (sequence, KV head) pairs.
+  // Aim for at least two (8-wave) workgroups per compute unit; longer
+  // partitions amortise each workgroup's start-up and the merge, shorter
+  // ones fill the chip when there are few (sequence, KV head) pairs.
   if (block_size <= 0) return 0;
   const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-  int p = 512;
-  while (p > 128 && pairs * ceil_div(max_seq_len > 0 ? max_seq_len : 1, p) < 4 * kCUs) p /= 2;
+  int p = pa::kMaxPartition;
+  while (p > 128 && pairs * ceil_div(max_seq_len > 0 ? max_seq_len : 1, p) < 2 * kCUs) p /= 2;
   if (p < block_size) p = block_size;
   return p - p % block_size;
 }

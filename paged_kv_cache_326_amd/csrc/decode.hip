@@ -6,7 +6,7 @@
 // table sits on chip; in-block reads coalesce) and "工程边界与架构取舍"
 // (decode is bound by reading the whole KV cache for one token).
 //
-// Work decomposition.  One workgroup of NW wavefronts handles one
+// Work decomposition.  One workgroup of NW (8) wavefronts handles one
 // (partition, KV head, sequence): a partition is `partition` consecutive
 // tokens of the sequence (a multiple of the block size).  All G query heads
 // that share the KV head are served by the same workgroup, so every K/V block
@@ -39,7 +39,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kNW = 4;  // wavefronts per workgroup
+constexpr int kNW = 8;  // wavefronts per workgroup (two workgroups per CU at 4 waves per SIMD)
 
 template <int G>
 struct Log2 {

@@ -83,7 +83,7 @@ def test_workspace_size_formula(L):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 16) == 2 * al(rows * 4) + al(rows * 64 * 4)
     assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 64) == 0  # one partition: written directly
-    assert L.pa_decode_auto_partition(16, 8, 4096, 16) in (128, 256, 512)
+    assert L.pa_decode_auto_partition(16, 8, 4096, 16) == 1024  # 16 x 8 pairs x 4 partitions = 2 per CU
     assert L.pa_decode_auto_partition(16, 8, 4096, 16) % 16 == 0
 
 
