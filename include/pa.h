@@ -70,6 +70,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3, /* head_dim / block_size / dtype / group size not built */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
   PA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
+  PA_ERR_NO_BLOCKS = 6,   /* block manager: the pool cannot supply the blocks (caller preempts) */
+  PA_ERR_NOT_FOUND = 7,   /* block manager: unknown sequence id */
+  PA_ERR_EXISTS = 8,      /* block manager: sequence id already in use */
 } pa_status;
 
 /* One layer's paged KV pool.  Both arrays are device memory owned by the
@@ -197,6 +200,68 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* quer
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            int32_t num_seqs, int32_t num_heads, int32_t max_q_len, float scale,
                            hipStream_t stream);
+
+/* Whole-block moves (K and V, all KV heads of a block; bit-exact copies).
+ * [P1] "KV Cache 的内存开销与分页机制": sequences may share a prefix's
+ * physical blocks; a sequence that must write into a shared, partly filled
+ * block first gets a private copy (pa_bm_append_tokens reports the pair).
+ * [P2] section 3.2: blocks can be moved out of HBM and back.
+ *
+ * pa_copy_blocks     pool block src[i] -> pool block dst[i], i < num_pairs
+ *                    (src, dst: device int32 arrays; dst must not repeat and
+ *                    must not be any src of the same call)
+ * pa_gather_blocks   pool block block_ids[i] -> row i of key_out/value_out
+ * pa_scatter_blocks  row i of key_in/value_in -> pool block block_ids[i]
+ * Buffers are [num_blocks][num_kv_heads][block_size][head_dim] in the cache
+ * dtype, device memory or pinned host memory (hipHostMalloc), so a gather or
+ * scatter through a pinned buffer swaps blocks out of or into HBM; other
+ * host memory is refused with PA_ERR_UNSUPPORTED.  Ids outside
+ * [0, cache->num_blocks) are skipped.
+ */
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src, const int32_t* dst,
+                         int32_t num_pairs, hipStream_t stream);
+pa_status pa_gather_blocks(const pa_kv_cache* cache, const int32_t* block_ids, int32_t num_blocks,
+                           void* key_out, void* value_out, hipStream_t stream);
+pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, int32_t num_blocks,
+                            const void* key_in, const void* value_in, hipStream_t stream);
+
+/* Host-side block manager (no device memory, thread-safe per manager).
+ * [P1] "生产级推理引擎的内存管理与调度": a FIFO pool of physical block ids,
+ * taken from the front and returned to the back; a sequence of n tokens owns
+ * ceil(n / block_size) blocks; when the pool cannot supply them the call
+ * fails with PA_ERR_NO_BLOCKS and changes nothing (the caller preempts).
+ * [P2] section 4.1: blocks shared by several sequences carry a reference
+ * count and return to the pool when the last reference is released.
+ *
+ * pa_bm_create          free_order: optional permutation of 0..num_blocks-1
+ *                       giving the initial free-list order (NULL = ascending);
+ *                       returns NULL on bad arguments
+ * pa_bm_add_sequence    new sequence holding num_tokens tokens
+ * pa_bm_fork            child shares all of parent's blocks (refcount + 1)
+ * pa_bm_append_tokens   grow by num_new tokens, taking blocks as needed; if
+ *                       the partly filled last block is shared it is replaced
+ *                       by a fresh block first and (old, new) is written to
+ *                       copy_src[0], copy_dst[0], *num_copies = 1 (else 0):
+ *                       copy it with pa_copy_blocks before scattering
+ * pa_bm_free_sequence   release every block reference of the sequence
+ * pa_bm_block_table     copies up to capacity entries; returns the table
+ *                       length (blocks), -1 if unknown
+ * pa_bm_free_list       copies up to capacity free ids in pool order;
+ *                       returns the number of free blocks
+ */
+typedef struct pa_block_manager pa_block_manager;
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pa_bm_destroy(pa_block_manager* bm);
+int32_t pa_bm_available(pa_block_manager* bm);
+int32_t pa_bm_refcount(pa_block_manager* bm, int32_t block);
+pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, int32_t num_tokens);
+pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+pa_status pa_bm_append_tokens(pa_block_manager* bm, int64_t seq_id, int32_t num_new, int32_t* copy_src,
+                              int32_t* copy_dst, int32_t* num_copies);
+pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
+int32_t pa_bm_block_table(pa_block_manager* bm, int64_t seq_id, int32_t* out, int32_t capacity);
+int64_t pa_bm_num_tokens(pa_block_manager* bm, int64_t seq_id);
+int32_t pa_bm_free_list(pa_block_manager* bm, int32_t* out, int32_t capacity);
 
 const char* pa_status_string(pa_status status);
 const char* pa_version(void);

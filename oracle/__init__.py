@@ -25,6 +25,8 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   decode_attention     torch SDPA (float64) on an identity-layout pool, closed
                        forms, block-permutation and shared-prefix invariance
   prefill_attention    torch SDPA causal / explicit-mask special cases
+  BlockPoolModel       FIFO order and conservation of blocks, reference
+                       counts under sharing, brute-force block counts
 No function here is "parity unpinned".
 """
 
@@ -37,3 +39,4 @@ from .paging import (  # noqa: F401
     gather_kv,
 )
 from .attention import decode_attention, prefill_attention  # noqa: F401
+from .block_pool import BlockPoolModel, NoBlocks, copy_blocks, gather_blocks, scatter_blocks  # noqa: F401

@@ -68,6 +68,9 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or head grouping";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks in the pool";
+    case PA_ERR_NOT_FOUND: return "unknown sequence id";
+    case PA_ERR_EXISTS: return "sequence id already in use";
   }
   return "unknown status";
 }
@@ -108,6 +111,54 @@ pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* va
   const hipError_t e = pa::launch_append(to_args(cache), key, value, block_tables, max_blocks_per_seq, seq_lens,
                                          cu_q_lens, num_seqs, max_q_len, slot_mapping, num_tokens, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// A staging buffer must be device memory or pinned host memory; the kernel
+// reaches pinned memory through its device mapping.  Pageable memory is
+// refused here rather than faulting in the kernel.
+static bool device_view(void** p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, *p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return true;
+  if (at.type != hipMemoryTypeHost) return false;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, *p, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return false;
+  }
+  *p = d;
+  return true;
+}
+
+static pa_status block_move(const pa_kv_cache* cache, const int32_t* a, const int32_t* b, void* kbuf, void* vbuf,
+                            int32_t n, int mode, hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (n == 0) return PA_OK;
+  if (!a || (mode == 0 && !b) || (mode != 0 && (!kbuf || !vbuf))) return PA_ERR_NULL;
+  if (mode != 0 && (!device_view(&kbuf) || !device_view(&vbuf))) return PA_ERR_UNSUPPORTED;
+  const hipError_t e = pa::launch_block_move(to_args(cache), a, b, kbuf, vbuf, n, mode, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                         hipStream_t stream) {
+  return block_move(cache, src, dst, nullptr, nullptr, num_pairs, 0, stream);
+}
+
+pa_status pa_gather_blocks(const pa_kv_cache* cache, const int32_t* block_ids, int32_t num_blocks, void* key_out,
+                           void* value_out, hipStream_t stream) {
+  return block_move(cache, block_ids, nullptr, key_out, value_out, num_blocks, 1, stream);
+}
+
+pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, int32_t num_blocks,
+                            const void* key_in, const void* value_in, hipStream_t stream) {
+  return block_move(cache, block_ids, nullptr, const_cast<void*>(key_in), const_cast<void*>(value_in), num_blocks, 2,
+                    stream);
 }
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {

@@ -142,6 +142,59 @@ hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* valu
   return hipErrorInvalidValue;
 }
 
+// Whole-block moves, 16 bytes per thread, K and V alike.  Mode 0: pool block
+// src[i] -> pool block dst[i] (copy-on-write); mode 1: pool block ids[i] ->
+// row i of a staging buffer; mode 2: row i of a staging buffer -> pool block
+// ids[i].  A staging buffer is [n][num_kv_heads][block_size][head_dim] and may
+// live in pinned host memory (then the move is a swap over the bus).  Block
+// ids outside the pool are skipped.
+__global__ void __launch_bounds__(256) block_move_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                         const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                                         uint8_t* __restrict__ kbuf, uint8_t* __restrict__ vbuf,
+                                                         int32_t n, int64_t block_bytes, int32_t num_blocks, int mode) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n * chunks * 2;
+  if (gid >= total) return;
+  const int which = (int)(gid / ((int64_t)n * chunks));  // 0 = K, 1 = V
+  const int64_t rem = gid - (int64_t)which * n * chunks;
+  const int i = (int)(rem / chunks);
+  const int64_t c = rem % chunks;
+  uint8_t* pool = which ? vc : kc;
+  uint8_t* buf = which ? vbuf : kbuf;
+  const uint8_t* from;
+  uint8_t* to;
+  if (mode == 0) {
+    const int32_t a = src[i], b = dst[i];
+    if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks || a == b) return;
+    from = pool + a * block_bytes;
+    to = pool + b * block_bytes;
+  } else if (mode == 1) {
+    const int32_t a = src[i];
+    if (a < 0 || a >= num_blocks) return;
+    from = pool + a * block_bytes;
+    to = buf + i * block_bytes;
+  } else {
+    const int32_t b = src[i];
+    if (b < 0 || b >= num_blocks) return;
+    from = buf + i * block_bytes;
+    to = pool + b * block_bytes;
+  }
+  reinterpret_cast<u32x4*>(to)[c] = reinterpret_cast<const u32x4*>(from)[c];
+}
+
+hipError_t launch_block_move(const KvCacheArgs& c, const int32_t* src, const int32_t* dst, void* kbuf, void* vbuf,
+                             int32_t n, int mode, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t eb = c.dtype == DType::kF32 ? 4 : 2;
+  const int64_t block_bytes = (int64_t)c.num_kv_heads * c.block_size * c.head_dim * eb;
+  const int64_t total = (int64_t)n * (block_bytes / 16) * 2;
+  hipLaunchKernelGGL(block_move_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     (uint8_t*)c.key_cache, (uint8_t*)c.value_cache, src, dst, (uint8_t*)kbuf, (uint8_t*)vbuf, n,
+                     block_bytes, c.num_blocks, mode);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                                const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
                                int64_t* slots, int32_t num_tokens, hipStream_t stream) {

@@ -59,6 +59,11 @@ hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* valu
                          int32_t max_blocks, const int32_t* seq_lens, const int32_t* cu_q_lens, int32_t num_seqs,
                          int32_t max_q_len, int64_t* slots, int32_t num_tokens, hipStream_t stream);
 
+// mode 0: pool -> pool (src[i] -> dst[i]); 1: pool src[i] -> buffer row i;
+// 2: buffer row i -> pool src[i].
+hipError_t launch_block_move(const KvCacheArgs& c, const int32_t* src, const int32_t* dst, void* kbuf, void* vbuf,
+                             int32_t n, int mode, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Query positions one prefill workgroup covers for a head group of `group`.

@@ -19,7 +19,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
-_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH"}
+_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH",
+           6: "PA_ERR_NO_BLOCKS", 7: "PA_ERR_NOT_FOUND", 8: "PA_ERR_EXISTS"}
+PA_ERR_NO_BLOCKS = 6
 
 
 class PaError(RuntimeError):
@@ -51,6 +53,20 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_ex",
     "pa_prefill_chunk",
+    "pa_copy_blocks",
+    "pa_gather_blocks",
+    "pa_scatter_blocks",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_available",
+    "pa_bm_refcount",
+    "pa_bm_add_sequence",
+    "pa_bm_fork",
+    "pa_bm_append_tokens",
+    "pa_bm_free_sequence",
+    "pa_bm_block_table",
+    "pa_bm_num_tokens",
+    "pa_bm_free_list",
     "pa_status_string",
     "pa_version",
 )
@@ -84,6 +100,36 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_ex.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [cache_p, vp, vp, i32p, i32p, i32p, i32, i32, i32, i32, f32, vp]
     L.pa_prefill_chunk.restype = ctypes.c_int
+    for name in ("pa_copy_blocks",):
+        getattr(L, name).argtypes = [cache_p, vp, vp, i32, vp]
+        getattr(L, name).restype = ctypes.c_int
+    for name in ("pa_gather_blocks", "pa_scatter_blocks"):
+        getattr(L, name).argtypes = [cache_p, vp, i32, vp, vp, vp]
+        getattr(L, name).restype = ctypes.c_int
+    bm = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    L.pa_bm_create.argtypes = [i32, i32, vp]
+    L.pa_bm_create.restype = bm
+    L.pa_bm_destroy.argtypes = [bm]
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_available.argtypes = [bm]
+    L.pa_bm_available.restype = i32
+    L.pa_bm_refcount.argtypes = [bm, i32]
+    L.pa_bm_refcount.restype = i32
+    L.pa_bm_add_sequence.argtypes = [bm, i64, i32]
+    L.pa_bm_add_sequence.restype = ctypes.c_int
+    L.pa_bm_fork.argtypes = [bm, i64, i64]
+    L.pa_bm_fork.restype = ctypes.c_int
+    L.pa_bm_append_tokens.argtypes = [bm, i64, i32, vp, vp, vp]
+    L.pa_bm_append_tokens.restype = ctypes.c_int
+    L.pa_bm_free_sequence.argtypes = [bm, i64]
+    L.pa_bm_free_sequence.restype = ctypes.c_int
+    L.pa_bm_block_table.argtypes = [bm, i64, vp, i32]
+    L.pa_bm_block_table.restype = i32
+    L.pa_bm_num_tokens.argtypes = [bm, i64]
+    L.pa_bm_num_tokens.restype = i64
+    L.pa_bm_free_list.argtypes = [bm, vp, i32]
+    L.pa_bm_free_list.restype = i32
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -226,6 +272,110 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, bl
                                 _stream(stream))
     _check(st, "pa_prefill_chunk")
     return out
+
+
+def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
+    """Pool block src[i] -> pool block dst[i] (device int32 tensors)."""
+    c = kv_cache(key_cache, value_cache)
+    _need(src, "src", torch.int32)
+    _need(dst, "dst", torch.int32)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must have the same length")
+    _check(lib().pa_copy_blocks(ctypes.byref(c), src.data_ptr(), dst.data_ptr(), src.numel(), _stream(stream)), "pa_copy_blocks")
+
+
+def _buf_ok(t, key_cache, n, name):
+    if t.dtype != key_cache.dtype or not t.is_contiguous() or tuple(t.shape) != (n, *key_cache.shape[1:]):
+        raise ValueError(f"{name} must be contiguous [{n}, *block shape] in the cache dtype")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be device memory or pinned host memory")
+
+
+def pa_gather_blocks(key_cache, value_cache, block_ids, key_out, value_out, stream=None):
+    c = kv_cache(key_cache, value_cache)
+    _need(block_ids, "block_ids", torch.int32)
+    n = block_ids.numel()
+    _buf_ok(key_out, key_cache, n, "key_out")
+    _buf_ok(value_out, key_cache, n, "value_out")
+    _check(lib().pa_gather_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_out.data_ptr(), value_out.data_ptr(),
+                                  _stream(stream)), "pa_gather_blocks")
+
+
+def pa_scatter_blocks(key_cache, value_cache, block_ids, key_in, value_in, stream=None):
+    c = kv_cache(key_cache, value_cache)
+    _need(block_ids, "block_ids", torch.int32)
+    n = block_ids.numel()
+    _buf_ok(key_in, key_cache, n, "key_in")
+    _buf_ok(value_in, key_cache, n, "value_in")
+    _check(lib().pa_scatter_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_in.data_ptr(), value_in.data_ptr(),
+                                   _stream(stream)), "pa_scatter_blocks")
+
+
+class BlockManager:
+    """The library's host-side block manager (FIFO pool, refcounts, copy-on-write)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        L = lib()
+        self._order = None
+        ptr = None
+        if free_order is not None:
+            import numpy as np
+
+            self._order = np.ascontiguousarray(free_order, dtype=np.int32)
+            ptr = self._order.ctypes.data
+        self._h = L.pa_bm_create(int(num_blocks), int(block_size), ptr)
+        if not self._h:
+            raise ValueError("pa_bm_create rejected its arguments")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        self._h = None
+        if h and _lib is not None:  # at interpreter exit the library may already be gone
+            _lib.pa_bm_destroy(h)
+
+    __del__ = close
+
+    def available(self) -> int:
+        return int(lib().pa_bm_available(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pa_bm_refcount(self._h, int(block)))
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        _check(lib().pa_bm_add_sequence(self._h, int(seq_id), int(num_tokens)), "pa_bm_add_sequence")
+
+    def fork(self, parent: int, child: int):
+        _check(lib().pa_bm_fork(self._h, int(parent), int(child)), "pa_bm_fork")
+
+    def append_tokens(self, seq_id: int, num_new: int):
+        """Returns the (src, dst) block pairs to copy before scattering."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_bm_append_tokens(self._h, int(seq_id), int(num_new), ctypes.addressof(src), ctypes.addressof(dst),
+                                         ctypes.addressof(n)), "pa_bm_append_tokens")
+        return [(src.value, dst.value)] if n.value else []
+
+    def free_sequence(self, seq_id: int):
+        _check(lib().pa_bm_free_sequence(self._h, int(seq_id)), "pa_bm_free_sequence")
+
+    def block_table(self, seq_id: int):
+        L = lib()
+        n = L.pa_bm_block_table(self._h, int(seq_id), None, 0)
+        if n < 0:
+            raise PaError(7, "pa_bm_block_table")
+        buf = (ctypes.c_int32 * max(n, 1))()
+        L.pa_bm_block_table(self._h, int(seq_id), buf, n)
+        return list(buf[:n])
+
+    def num_tokens(self, seq_id: int) -> int:
+        return int(lib().pa_bm_num_tokens(self._h, int(seq_id)))
+
+    def free_list(self):
+        L = lib()
+        n = L.pa_bm_free_list(self._h, None, 0)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        L.pa_bm_free_list(self._h, buf, n)
+        return list(buf[:n])
 
 
 def version() -> str:
