@@ -53,12 +53,74 @@ def measured_traffic():
     return int(rec["bytes_per_call"])
 
 
-def algorithmic_decode_bytes(w) -> int:
+COPY_CALIBRATION_MIB = 1024
+
+
+def write_traffic_record(pmc_dir: str):
+    """Turn four rocprofv3 --pmc runs (under pmc_dir: pmc_fetch, pmc_write of
+    the default benchmark; pmc_copy_fetch, pmc_copy_write of
+    --calibrate-copy 1024) into the traffic record: FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch) scaled by what they read for a plain copy of known
+    size, per decode call."""
+    import csv
+    import hashlib
+
+    from paged_kv_cache_326_amd import synth
+
+    def mean(sub, match):
+        with open(os.path.join(pmc_dir, sub, "run_counter_collection.csv")) as f:
+            v = [float(r["Counter_Value"]) for r in csv.DictReader(f) if match(r["Kernel_Name"])]
+        if not v:
+            raise SystemExit(f"no matching dispatch in {sub}")
+        return sum(v) / len(v)
+
+    nbytes = COPY_CALIBRATION_MIB << 20
+    copy = lambda n: "copyBuffer" in n  # noqa: E731
+    cf, cw = mean("pmc_copy_fetch", copy), mean("pmc_copy_write", copy)
+    ff, wf = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    part = lambda n: "decode_partition_kernel" in n and "DF16_Li128ELi16ELi8" in n  # noqa: E731
+    merge = lambda n: "decode_reduce_kernel" in n  # noqa: E731
+    rec = {
+        "what": "HBM bytes per pa_decode call (partition + merge kernels), 16 x 4096-token LLaMA-2-70B-shaped "
+                "layer, fp16, automatic partition",
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py "
+            "--steps 5 --warmup 2 --no-cpu-baseline --no-secondary",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py "
+            "--steps 5 --warmup 2 --no-cpu-baseline --no-secondary",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o run -- python3 bench.py "
+            f"--calibrate-copy {COPY_CALIBRATION_MIB} --steps 3",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o run -- python3 bench.py "
+            f"--calibrate-copy {COPY_CALIBRATION_MIB} --steps 3",
+            "python3 bench.py --write-traffic-record gpurun_out",
+        ],
+        "calibration": {"copy_bytes_each_way": nbytes, "copy_FETCH_SIZE_KiB": round(cf, 1),
+                        "copy_WRITE_SIZE_KiB": round(cw, 1), "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+    }
+    total = 0
+    for name, match in (("partition_kernel", part), ("merge_kernel", merge)):
+        f, wr = mean("pmc_fetch", match), mean("pmc_write", match)
+        b = int(round((f * ff + wr * wf) * 1024))
+        rec[name] = {"FETCH_SIZE_KiB": round(f, 1), "WRITE_SIZE_KiB": round(wr, 1), "bytes": b}
+        total += b
+    alg = algorithmic_decode_bytes(synth.config(2, poison_unused=False))
+    rec["bytes_per_call"] = total
+    rec["algorithmic_bytes_per_call"] = alg
+    rec["ratio_to_algorithmic"] = round(total / alg, 4)
+    rec["decode_source_sha256"] = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def algorithmic_decode_bytes(w, kv_elem_bytes=None) -> int:
     """K+V of every attended token, query in, output out, the block-table
-    entries actually read, and seq_lens."""
+    entries actually read, and seq_lens.  ``kv_elem_bytes`` = 1 for an FP8
+    pool (its queries and outputs stay 16-bit)."""
     dt = w.elem_bytes
     B = w.block_size
-    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * dt * 2
+    kvb = dt if kv_elem_bytes is None else kv_elem_bytes
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * kvb * 2
     qo = 2 * w.num_seqs * w.num_heads * w.head_dim * dt
     bt = int(sum(-(-int(L) // B) for L in w.seq_lens)) * 4
     return kv + qo + bt + 4 * w.num_seqs
@@ -160,6 +222,34 @@ def secondary(copies_n: int):
         "permuted_us": round(out["permuted"], 2), "identity_us": round(out["identity"], 2),
         "overhead_pct": round(100.0 * (out["permuted"] / out["identity"] - 1.0), 2),
     }
+    # The benchmark layer over an FP8 (E4M3) pool: the same float16 rows
+    # quantised by the library's scatter, per-tensor scales.
+    from tests import harness
+
+    scales = (0.0173, 0.0291)
+    cs = _copies(w, copies_n)
+    pools = []
+    for c in cs:
+        kc8, vc8 = harness.fp8_pool_gpu(c, scales)
+        pools.append((c, kc8, vc8, pa.decode_workspace(c.query, kc8, w.max_seq_len)))
+        c.key_cache = c.value_cache = None  # the 16-bit pool is no longer needed
+    torch.cuda.empty_cache()
+
+    def fp8_decode(i):
+        c, kc8, vc8, ws = pools[i % len(pools)]
+        pa.pa_decode(c.out, c.query, kc8, vc8, c.block_tables, c.seq_lens, w.scale, w.max_seq_len, workspace=ws,
+                     scales=scales)
+
+    t8 = _median_us(fp8_decode)
+    nb8 = algorithmic_decode_bytes(w, kv_elem_bytes=1)
+    res["fp8_e4m3_" + synth.CONFIG_NAMES[2]] = {
+        "decode_us": round(t8, 2), "algorithmic_bytes": nb8, "GBps": round(nb8 / t8 / 1e3, 1),
+        "frac_of_hbm_peak": round(nb8 / t8 / 1e3 / HBM_PEAK_GBS, 4),
+        "attended_tokens_per_s": int(w.seq_lens.sum()) / (t8 * 1e-6),
+        "speedup_vs_f16": round(out["permuted"] / t8, 3), "scales": list(scales),
+    }
+    del cs, pools
+    torch.cuda.empty_cache()
     return res
 
 
@@ -213,8 +303,13 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--write-traffic-record", metavar="DIR", default=None,
+                    help="instead: build the traffic record from the --pmc runs under DIR (no GPU needed)")
     args = ap.parse_args()
 
+    if args.write_traffic_record:
+        write_traffic_record(args.write_traffic_record)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the decode shards by "
               "sequence or KV head with no exchange; see the design notes)", file=sys.stderr)

@@ -57,10 +57,16 @@
 extern "C" {
 #endif
 
+/* Storage dtype of a pool.  PA_FP8_E4M3 stores OCP E4M3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; largest finite
+ * 448) under one float32 scale per pool: [P1] "工程边界与架构取舍" names
+ * FP8 KV quantisation as the conservative way to halve KV memory.  Its
+ * queries, outputs and new K/V rows are float16. */
 typedef enum {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
+  PA_FP8_E4M3 = 3,
 } pa_dtype;
 
 typedef enum {
@@ -76,7 +82,11 @@ typedef enum {
 } pa_status;
 
 /* One layer's paged KV pool.  Both arrays are device memory owned by the
- * caller, shape [num_blocks][num_kv_heads][block_size][head_dim], `dtype`. */
+ * caller, shape [num_blocks][num_kv_heads][block_size][head_dim], `dtype`.
+ * k_scale and v_scale are read only for PA_FP8_E4M3 (must then be positive
+ * and finite, else PA_ERR_SHAPE): a key code c stands for value(c) * k_scale,
+ * a value code for value(c) * v_scale.  New rows are quantised as
+ * round-to-nearest-even(x / scale) in float32, saturating at +-448. */
 typedef struct {
   void* key_cache;
   void* value_cache;
@@ -85,6 +95,8 @@ typedef struct {
   int32_t head_dim;
   int32_t block_size;
   pa_dtype dtype;
+  float k_scale;
+  float v_scale;
 } pa_kv_cache;
 
 /* Slot of every new token.  [P1] "KV Cache 的内存开销与分页机制": a token at
@@ -111,7 +123,8 @@ pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_se
  * [P1] "KV Cache 的内存开销与分页机制": the new token's vectors are stored in
  * the current block, or in a block appended to the table when it is full.
  *
- * key, value    [num_tokens][num_kv_heads][head_dim], cache->dtype
+ * key, value    [num_tokens][num_kv_heads][head_dim], cache->dtype (float16
+ *               for an FP8 pool, which stores the quantised codes)
  * slot_mapping  int64 [num_tokens]; a negative slot marks a padding token and
  *               is skipped.  Two tokens must not share a slot.
  */
@@ -154,8 +167,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *     out[s][h] = softmax_t(scale * q[s][h] . K[s][t][g]) . V[s][t][g],
  * t over 0 .. seq_lens[s]-1; a sequence of length 0 yields zeros.
  *
- * out, query    [num_seqs][num_heads][head_dim], cache->dtype (out is
- *               rounded from float32 to nearest-even)
+ * out, query    [num_seqs][num_heads][head_dim], cache->dtype, float16 for
+ *               an FP8 pool (out is rounded from float32 to nearest-even).
+ *               An FP8 pool needs head_dim 128 (else PA_ERR_UNSUPPORTED); its
+ *               codes are widened exactly to float16 in registers and the
+ *               scales applied to the float32 logits and outputs.
  * max_seq_len   host-side upper bound of seq_lens (<= max_blocks_per_seq *
  *               block_size); longer device values are clamped to it
  * workspace     device scratch of at least pa_decode_workspace_bytes(); may
@@ -188,7 +204,8 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query,
  *     out[t][h] = softmax_j(scale * q[t][h] . K[s][j]) . V[s][j],  j <= ctx+i.
  *
  * out, query   [cu_q_lens[num_seqs]][num_heads][head_dim], cache->dtype
- *              (f16 or bf16; rounded to nearest-even)
+ *              (f16 or bf16; rounded to nearest-even; other pool dtypes
+ *              return PA_ERR_UNSUPPORTED)
  * cu_q_lens    int32 [num_seqs + 1]
  * seq_lens     int32 [num_seqs], >= the sequence's chunk length
  * max_q_len    host-side upper bound of the chunk lengths

@@ -22,7 +22,13 @@ pa_status check_cache(const pa_kv_cache* c) {
   if (!c || !c->key_cache || !c->value_cache) return PA_ERR_NULL;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
   if (!supported_shape(c->head_dim, c->block_size)) return PA_ERR_UNSUPPORTED;
-  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3)
+    return PA_ERR_UNSUPPORTED;
+  if (c->dtype == PA_FP8_E4M3) {
+    // Positive and finite (a NaN fails both comparisons).
+    if (!(c->k_scale > 0.f && c->k_scale <= 3.4e38f) || !(c->v_scale > 0.f && c->v_scale <= 3.4e38f))
+      return PA_ERR_SHAPE;
+  }
   return PA_OK;
 }
 
@@ -35,6 +41,8 @@ pa::KvCacheArgs to_args(const pa_kv_cache* c) {
   a.head_dim = c->head_dim;
   a.block_size = c->block_size;
   a.dtype = static_cast<pa::DType>(c->dtype);
+  a.k_scale = c->dtype == PA_FP8_E4M3 ? c->k_scale : 1.f;
+  a.v_scale = c->dtype == PA_FP8_E4M3 ? c->v_scale : 1.f;
   return a;
 }
 
@@ -64,7 +72,7 @@ const char* pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
-    case PA_ERR_SHAPE: return "inconsistent sizes";
+    case PA_ERR_SHAPE: return "inconsistent sizes or an invalid scale";
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or head grouping";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
@@ -192,6 +200,7 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, c
   if (!supported_group(num_heads, cache->num_kv_heads)) {
     return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
   }
+  if (cache->dtype == PA_FP8_E4M3 && cache->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
   int p = partition_size;
   if (p == 0) p = pa_decode_auto_partition(num_seqs, cache->num_kv_heads, max_seq_len, cache->block_size);

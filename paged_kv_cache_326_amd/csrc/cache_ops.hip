@@ -34,16 +34,52 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(
   }
 }
 
+// New K/V rows are stored as they come, except into an FP8 pool, whose rows
+// arrive as float16 and are quantised on the way: code = E4M3(x / scale),
+// the division in float32 (IEEE, rounded to nearest).
+template <typename T>
+struct Src {
+  using type = T;
+};
+template <>
+struct Src<fp8_t> {
+  using type = f16_t;
+};
+
+// Store the VEC = vec16<Src<T>> source elements of one 16-byte chunk.
+template <typename T>
+__device__ __forceinline__ void store_chunk(T* dst, const u32x4& data, float) {
+  *reinterpret_cast<u32x4*>(dst) = data;
+}
+template <>
+__device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4& data, float scale) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t word = data[2 * i + j];
+      const uint32_t lo = f32_to_e4m3(f16_lo(word) / scale);
+      const uint32_t hi = f32_to_e4m3(f16_hi(word) / scale);
+      acc |= (lo | (hi << 8)) << (16 * j);
+    }
+    w[i] = acc;
+  }
+  *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+}
+
 // Each thread moves one 16-byte chunk of one token's K or V row.  A token row
 // of one KV head is head_dim elements; the pool tile of (block, KV head) is
 // [block_size][head_dim], so the destination of (token, head) is
 //   ((block * num_kv_heads + head) * block_size + offset) * head_dim.
 template <typename T>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
-    T* __restrict__ key_cache, T* __restrict__ value_cache, const T* __restrict__ key,
-    const T* __restrict__ value, const int64_t* __restrict__ slots, int32_t num_tokens,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t pool_slots) {
-  constexpr int VEC = vec16<T>();
+    T* __restrict__ key_cache, T* __restrict__ value_cache, const typename Src<T>::type* __restrict__ key,
+    const typename Src<T>::type* __restrict__ value, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t pool_slots, float k_scale, float v_scale) {
+  using S = typename Src<T>::type;
+  constexpr int VEC = vec16<S>();
   const int chunks_per_row = head_dim / VEC;          // 16-byte chunks per head row
   const int chunks_per_tok = num_kv_heads * chunks_per_row;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -59,10 +95,10 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
   const int ch = c % chunks_per_row;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot % block_size);
-  const T* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
+  const S* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
   T* dst = (which ? value_cache : key_cache) +
            ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
-  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  store_chunk<T>(dst, *reinterpret_cast<const u32x4*>(src), which ? v_scale : k_scale);
 }
 
 // Slot mapping and scatter in one pass.  Workgroup (x, s) covers new tokens
@@ -74,11 +110,13 @@ constexpr int kAppendTok = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(256) append_kernel(
-    T* __restrict__ key_cache, T* __restrict__ value_cache, const T* __restrict__ key,
-    const T* __restrict__ value, const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    T* __restrict__ key_cache, T* __restrict__ value_cache, const typename Src<T>::type* __restrict__ key,
+    const typename Src<T>::type* __restrict__ value, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q_lens, int64_t* __restrict__ slots,
-    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks) {
-  constexpr int VEC = vec16<T>();
+    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    float k_scale, float v_scale) {
+  using S = typename Src<T>::type;
+  constexpr int VEC = vec16<S>();
   const int s = blockIdx.y;
   const int t0 = cu_q_lens[s];
   const int q = cu_q_lens[s + 1] - t0;
@@ -95,7 +133,7 @@ __global__ void __launch_bounds__(256) append_kernel(
     const int which = c / (num_kv_heads * chunks_per_row);
     const int h = (c / chunks_per_row) % num_kv_heads;
     const int ch = c % chunks_per_row;
-    const T* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
+    const S* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
     const u32x4 data = *reinterpret_cast<const u32x4*>(src);
     const int pos = L - q + i;
     int64_t slot = -1, phys = -1;
@@ -108,7 +146,7 @@ __global__ void __launch_bounds__(256) append_kernel(
     const int64_t blk = slot / block_size;
     const int off = (int)(slot % block_size);
     T* dst = (which ? value_cache : key_cache) + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
-    *reinterpret_cast<u32x4*>(dst) = data;
+    store_chunk<T>(dst, data, which ? v_scale : k_scale);
   }
 }
 
@@ -119,9 +157,10 @@ static hipError_t launch_append_t(const KvCacheArgs& c, const void* key, const v
                                   int32_t num_tokens, hipStream_t stream) {
   if (num_seqs == 0 || max_q_len == 0) return hipSuccess;
   dim3 grid((max_q_len + kAppendTok - 1) / kAppendTok, num_seqs);
-  hipLaunchKernelGGL(append_kernel<T>, grid, dim3(256), 0, stream, (T*)c.key_cache, (T*)c.value_cache, (const T*)key,
-                     (const T*)value, block_tables, max_blocks, seq_lens, cu_q_lens, slots, num_tokens, c.num_kv_heads,
-                     c.head_dim, c.block_size, c.num_blocks);
+  using S = typename Src<T>::type;
+  hipLaunchKernelGGL(append_kernel<T>, grid, dim3(256), 0, stream, (T*)c.key_cache, (T*)c.value_cache, (const S*)key,
+                     (const S*)value, block_tables, max_blocks, seq_lens, cu_q_lens, slots, num_tokens, c.num_kv_heads,
+                     c.head_dim, c.block_size, c.num_blocks, c.k_scale, c.v_scale);
   return hipGetLastError();
 }
 
@@ -138,6 +177,9 @@ hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* valu
     case DType::kBF16:
       return launch_append_t<bf16_t>(c, key, value, block_tables, max_blocks, seq_lens, cu_q_lens, num_seqs,
                                      max_q_len, slots, num_tokens, stream);
+    case DType::kFP8:
+      return launch_append_t<fp8_t>(c, key, value, block_tables, max_blocks, seq_lens, cu_q_lens, num_seqs,
+                                    max_q_len, slots, num_tokens, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -186,7 +228,7 @@ __global__ void __launch_bounds__(256) block_move_kernel(uint8_t* __restrict__ k
 hipError_t launch_block_move(const KvCacheArgs& c, const int32_t* src, const int32_t* dst, void* kbuf, void* vbuf,
                              int32_t n, int mode, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t eb = c.dtype == DType::kF32 ? 4 : 2;
+  const int64_t eb = c.dtype == DType::kF32 ? 4 : c.dtype == DType::kFP8 ? 1 : 2;
   const int64_t block_bytes = (int64_t)c.num_kv_heads * c.block_size * c.head_dim * eb;
   const int64_t total = (int64_t)n * (block_bytes / 16) * 2;
   hipLaunchKernelGGL(block_move_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
@@ -207,13 +249,15 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, 
 template <typename T>
 static hipError_t launch_rac(const KvCacheArgs& c, const void* key, const void* value, const int64_t* slots,
                              int32_t num_tokens, hipStream_t stream) {
-  constexpr int VEC = vec16<T>();
+  using S = typename Src<T>::type;
+  constexpr int VEC = vec16<S>();
   const int64_t total = (int64_t)num_tokens * c.num_kv_heads * (c.head_dim / VEC) * 2;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(reshape_and_cache_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (T*)c.key_cache, (T*)c.value_cache, (const T*)key, (const T*)value, slots, num_tokens,
-                     c.num_kv_heads, c.head_dim, c.block_size, (int64_t)c.num_blocks * c.block_size);
+                     (T*)c.key_cache, (T*)c.value_cache, (const S*)key, (const S*)value, slots, num_tokens,
+                     c.num_kv_heads, c.head_dim, c.block_size, (int64_t)c.num_blocks * c.block_size, c.k_scale,
+                     c.v_scale);
   return hipGetLastError();
 }
 
@@ -226,6 +270,8 @@ hipError_t launch_reshape_and_cache(const KvCacheArgs& c, const void* key, const
       return launch_rac<f16_t>(c, key, value, slots, num_tokens, stream);
     case DType::kBF16:
       return launch_rac<bf16_t>(c, key, value, slots, num_tokens, stream);
+    case DType::kFP8:
+      return launch_rac<fp8_t>(c, key, value, slots, num_tokens, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -79,6 +79,50 @@ __device__ __forceinline__ float dot16<float>(const u32x4& q, const u32x4& k, fl
   return acc;
 }
 
+// Query/output type of a pool dtype: FP8 pools take float16 queries.
+template <typename T>
+struct QType {
+  using type = T;
+};
+template <>
+struct QType<fp8_t> {
+  using type = f16_t;
+};
+
+// A 16-byte K chunk as dot-product operands in the query type: itself, or
+// for FP8 its 16 codes widened to two chunks of f16 pairs (values * 2^-8,
+// exact; the 2^8 goes into the logit scale).
+template <typename T>
+struct KOps {
+  static constexpr int kW = 1;
+  __device__ static __forceinline__ void widen(const u32x4& k, u32x4* out) { out[0] = k; }
+};
+template <>
+struct KOps<fp8_t> {
+  static constexpr int kW = 2;
+  __device__ static __forceinline__ void widen(const u32x4& k, u32x4* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = k[i];
+      out[i / 2][2 * (i % 2)] = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes01));
+      out[i / 2][2 * (i % 2) + 1] = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes23));
+    }
+  }
+};
+
+// V chunk one PV lane loads per token: 16 bytes, or 8 for FP8 (8 dims, so
+// that the lane's accumulators stay G * 8).
+template <typename T>
+struct VOps {
+  typedef u32x4 load_t;
+  static constexpr int kDims = vec16<T>();
+};
+template <>
+struct VOps<fp8_t> {
+  typedef u32x2 load_t;
+  static constexpr int kDims = 8;
+};
+
 // 16 bytes of storage -> VEC floats.
 template <typename T>
 __device__ __forceinline__ void unpack16(const u32x4& v, float* f);
@@ -246,15 +290,20 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
 
 template <typename T, int G>
 struct Occupancy {
-  // 2-byte types fit in 128 VGPRs (4 waves per SIMD); f32 is a correctness
-  // path and keeps the compiler's choice.
-  static constexpr int kWaves = Elem<T>::kBytes == 2 ? 4 : 1;
+  // 1- and 2-byte types fit in 128 VGPRs (4 waves per SIMD); f32 is a
+  // correctness path and keeps the compiler's choice.
+  static constexpr int kWaves = Elem<T>::kBytes <= 2 ? 4 : 1;
 };
 
 template <typename T, int D, int B, int G>
 __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(Occupancy<T, G>::kWaves)))
 decode_partition_kernel(DecodeArgs a) {
-  constexpr int VEC = vec16<T>();
+  using QT = typename QType<T>::type;
+  using VLoad = typename VOps<T>::load_t;
+  constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
+  constexpr int VEC = vec16<T>();   // K dims per 16-byte load
+  constexpr int QVEC = vec16<QT>(); // query elements per 16 bytes
+  constexpr int KW = KOps<T>::kW;   // operand chunks per K chunk
   constexpr int LPT = 8;            // lanes per token (QK)
   constexpr int DL = D / LPT;       // dims per lane (QK)
   constexpr int NCK = DL / VEC;     // 16-byte chunks per lane per token (QK)
@@ -262,12 +311,13 @@ decode_partition_kernel(DecodeArgs a) {
   constexpr int CPB = B / CH;       // chunks per block
   constexpr int TPG = 64 / LPT;     // tokens per load group (QK)
   constexpr int GPC = CH / TPG;     // load groups per chunk (QK)
-  constexpr int LPV = D / VEC;      // lanes per token (PV)
+  constexpr int VV = VOps<T>::kDims; // dims per lane (PV)
+  constexpr int LPV = D / VV;       // lanes per token (PV)
   constexpr int TS = 64 / LPV;      // token slots per load (PV)
   constexpr int IPC = CH / TS;      // loads per chunk (PV)
   constexpr int NT = kNW * 64;
   constexpr int SHIFT = 3 - Log2<G>::v;
-  constexpr int NV = G * VEC;       // PV accumulators per lane
+  constexpr int NV = G * VV;        // PV accumulators per lane
   static_assert(B % CH == 0 && NCK >= 1 && GPC >= 1 && IPC >= 1, "unsupported shape");
   static_assert(64 % G == 0, "group size must divide the wave");
 
@@ -315,7 +365,7 @@ decode_partition_kernel(DecodeArgs a) {
   // dword per (pair, head), pair index jc*CH/2 + (i/2)*TS + ts for the token
   // loaded by PV load i of chunk jc in slot ts.
   uint32_t* s_h = reinterpret_cast<uint32_t*>(smem + lay.h_off) + w * lay.h_wave;
-  constexpr bool kDot2PV = std::is_same<T, f16_t>::value;
+  constexpr bool kDot2PV = std::is_same<QT, f16_t>::value;
   // Wave w's partial output, once its PV pass is done: [G][D] floats at the
   // start of region w.
   float* s_o = reinterpret_cast<float*>(smem + lay.p_off);
@@ -328,11 +378,11 @@ decode_partition_kernel(DecodeArgs a) {
   // The G query rows of this KV head are fetched once per workgroup into LDS
   // (G*D elements, 16 bytes per thread); every lane then reads its slices
   // from there, eight lanes per address.
-  T* s_q = reinterpret_cast<T*>(smem + lay.q_off);
+  QT* s_q = reinterpret_cast<QT*>(smem + lay.q_off);
   {
-    const T* qb = reinterpret_cast<const T*>(a.query) + ((int64_t)s * Hq + g * G) * D;
-    for (int c = tid; c < G * D / VEC; c += NT)
-      *reinterpret_cast<u32x4*>(s_q + c * VEC) = *reinterpret_cast<const u32x4*>(qb + c * VEC);
+    const QT* qb = reinterpret_cast<const QT*>(a.query) + ((int64_t)s * Hq + g * G) * D;
+    for (int c = tid; c < G * D / QVEC; c += NT)
+      *reinterpret_cast<u32x4*>(s_q + c * QVEC) = *reinterpret_cast<const u32x4*>(qb + c * QVEC);
   }
   __syncthreads();
 
@@ -340,19 +390,22 @@ decode_partition_kernel(DecodeArgs a) {
   // head, dims c*LPT*VEC + sub*VEC .. +VEC of every chunk c.
   const int sub = lane & (LPT - 1);
   const int tq = lane / LPT;
-  u32x4 qv[G][NCK];
+  u32x4 qv[G][NCK * KW];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int c = 0; c < NCK; ++c)
-      qv[h][c] = *reinterpret_cast<const u32x4*>(s_q + h * D + c * LPT * VEC + sub * VEC);
+#pragma unroll
+      for (int w2 = 0; w2 < KW; ++w2)
+        qv[h][c * KW + w2] = *reinterpret_cast<const u32x4*>(s_q + h * D + c * LPT * VEC + sub * VEC + w2 * QVEC);
 
   // This wave's blocks: local index jl -> partition block w + jl*NW.
   const int nbw = nblk > w ? (nblk - w + kNW - 1) / kNW : 0;
   const int64_t blk_stride = (int64_t)Hkv * B * D;
   const T* kbase = reinterpret_cast<const T*>(a.cache.key_cache) + (int64_t)g * B * D;
   const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * B * D;
-  const float qscale = a.scale * kLog2e;
+  // FP8: widened K values are the codes' values * 2^-8.
+  const float qscale = kFp8 ? a.scale * kLog2e * 256.f * a.cache.k_scale : a.scale * kLog2e;
   const int myhead = sub >> SHIFT;
   const bool writer = (sub & ((1 << SHIFT) - 1)) == 0;
 
@@ -384,12 +437,15 @@ decode_partition_kernel(DecodeArgs a) {
     const bool valid = chunk_src(kbase, jc, t0) != nullptr;
 #pragma unroll
     for (int gi = 0; gi < GPC; ++gi) {
+      u32x4 ko[NCK * KW];
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) KOps<T>::widen(kb[gi][c], ko + c * KW);
       float acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < NCK; ++c) x = dot16<T>(qv[h][c], kb[gi][c], x);
+        for (int c = 0; c < NCK * KW; ++c) x = dot16<QT>(qv[h][c], ko[c], x);
         acc[h] = x;
       }
       float z = reduce_scatter8<G>(acc, sub);
@@ -411,17 +467,17 @@ decode_partition_kernel(DecodeArgs a) {
   }
 
   // The first V chunk goes out before the softmax so HBM stays busy.
-  auto v_load = [&](u32x4 (&vb)[IPC], int jc) {
+  auto v_load = [&](VLoad (&vb)[IPC], int jc) {
     int t0;
     const T* src = chunk_src(vbase, jc, t0);
     if (src) {
       const int ts = lane / LPV, dc = lane % LPV;
 #pragma unroll
       for (int i = 0; i < IPC; ++i)
-        vb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (i * TS + ts) * D + dc * VEC));
+        vb[i] = __builtin_nontemporal_load(reinterpret_cast<const VLoad*>(src + (i * TS + ts) * D + dc * VV));
     }
   };
-  u32x4 vb0[IPC], vb1[IPC];
+  VLoad vb0[IPC], vb1[IPC];
   if (nch > 0) v_load(vb0, 0);
 
   // 3. Wave-local softmax.  Lanes with equal `sub` hold the same head.
@@ -462,7 +518,7 @@ decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < NV; ++k) o[k] = 0.f;
   const int ts = lane / LPV;
-  auto pv_block = [&](const u32x4 (&vb)[IPC], int jc) {
+  auto pv_block = [&](const VLoad (&vb)[IPC], int jc) {
     int t0;
     if (!chunk_src(vbase, jc, t0)) return;
     if constexpr (kDot2PV) {
@@ -470,17 +526,29 @@ decode_partition_kernel(DecodeArgs a) {
       // halves with v_perm and dot them with the packed (p_t0, p_t1).
 #pragma unroll
       for (int i = 0; i < IPC; i += 2) {
-        u32x4 va = vb[i], vz = vb[i + 1];
+        VLoad va = vb[i], vz = vb[i + 1];
         // Tail of the last block: zero V of tokens past the end (p is 0
         // there, and 0 * NaN would poison the sum).
-        if (t0 + i * TS + ts >= ntok) va = u32x4{0, 0, 0, 0};
-        if (t0 + (i + 1) * TS + ts >= ntok) vz = u32x4{0, 0, 0, 0};
-        uint32_t X[VEC];
+        if (t0 + i * TS + ts >= ntok) va = VLoad(0u);
+        if (t0 + (i + 1) * TS + ts >= ntok) vz = VLoad(0u);
+        uint32_t X[VV];
+        if constexpr (kFp8) {
+          // Byte j of each token's word -> bits 15:8 / 31:24, then widen.
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = va[q], hi = vz[q];
-          X[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-          X[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t lo = va[q], hi = vz[q];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              X[4 * q + j] = e4m3_pair_to_f16x2(
+                  __builtin_amdgcn_perm(hi, lo, ((4u + j) << 24) | (0x0cu << 16) | ((uint32_t)j << 8) | 0x0cu));
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = va[q], hi = vz[q];
+            X[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            X[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          }
         }
         const int pair = jc * (CH / 2) + (i / 2) * TS + ts;
         uint32_t pw[G];
@@ -499,12 +567,11 @@ decode_partition_kernel(DecodeArgs a) {
         for (int h = 0; h < G; ++h) {
           const f16x2 ph = __builtin_bit_cast(f16x2, pw[h]);
 #pragma unroll
-          for (int v = 0; v < VEC; ++v)
-            o[h * VEC + v] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(f16x2, X[v]), o[h * VEC + v], false);
+          for (int v = 0; v < VV; ++v)
+            o[h * VV + v] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(f16x2, X[v]), o[h * VV + v], false);
         }
       }
-      return;
-    }
+    } else {
 #pragma unroll
     for (int i = 0; i < IPC; ++i) {
       const int tb = i * TS + ts;  // token within the chunk
@@ -521,12 +588,13 @@ decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) pr[h] = pp[h];
       }
-      float vf[VEC];
+      float vf[VV];
       unpack16<T>(vb[i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) o[h * VEC + v] = fmaf(pr[h], vf[v], o[h * VEC + v]);
+        for (int v = 0; v < VV; ++v) o[h * VV + v] = fmaf(pr[h], vf[v], o[h * VV + v]);
+    }
     }
   };
   for (int jc = 0; jc < nch; jc += 2) {
@@ -548,8 +616,8 @@ decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int k = q * PER + j;
-        const int h = k / VEC, v = k % VEC;
-        s_o[w * lay.p_wave + h * D + col * VEC + v] = o[j];
+        const int h = k / VV, v = k % VV;
+        s_o[w * lay.p_wave + h * D + col * VV + v] = o[j];
       }
     }
   }
@@ -559,6 +627,8 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
+  // FP8: widened V values are the codes' values * 2^-8.
+  const float vfac = kFp8 ? 256.f * a.cache.v_scale : 1.f;
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D;
     const int d = idx % D;
@@ -576,9 +646,10 @@ decode_partition_kernel(DecodeArgs a) {
       }
     }
     const int hq = g * G + h;
+    acc *= vfac;
     if (direct) {
-      T* out = reinterpret_cast<T*>(a.out) + ((int64_t)s * Hq + hq) * D + d;
-      store_elem<T>(out, l > 0.f ? acc / l : 0.f);
+      QT* out = reinterpret_cast<QT*>(a.out) + ((int64_t)s * Hq + hq) * D + d;
+      store_elem<QT>(out, l > 0.f ? acc / l : 0.f);
     } else {
       const int64_t row = ((int64_t)s * Hq + hq) * a.num_partitions + part;
       a.ws_o[row * D + d] = acc;
@@ -613,7 +684,8 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_seq_len > a.partition) {
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
+                       stream, a);
     e = hipGetLastError();
   }
   return e;
@@ -641,11 +713,16 @@ hipError_t dispatch_b(const DecodeArgs& a, int G, hipStream_t stream) {
 
 template <typename T>
 hipError_t dispatch_d(const DecodeArgs& a, int G, hipStream_t stream) {
-  switch (a.cache.head_dim) {
-    case 64: return dispatch_b<T, 64>(a, G, stream);
-    case 128: return dispatch_b<T, 128>(a, G, stream);
+  if constexpr (Elem<T>::kBytes == 1) {
+    // 16 codes per lane per token need 8 x 16 = 128 dims.
+    return a.cache.head_dim == 128 ? dispatch_b<T, 128>(a, G, stream) : hipErrorInvalidValue;
+  } else {
+    switch (a.cache.head_dim) {
+      case 64: return dispatch_b<T, 64>(a, G, stream);
+      case 128: return dispatch_b<T, 128>(a, G, stream);
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -661,6 +738,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     case DType::kF32: return dispatch_d<float>(a, G, stream);
     case DType::kF16: return dispatch_d<f16_t>(a, G, stream);
     case DType::kBF16: return dispatch_d<bf16_t>(a, G, stream);
+    case DType::kFP8: return dispatch_d<fp8_t>(a, G, stream);
   }
   return hipErrorInvalidValue;
 }

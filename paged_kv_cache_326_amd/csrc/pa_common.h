@@ -13,6 +13,10 @@ struct bf16_t {
   uint16_t bits;
 };
 typedef _Float16 f16_t;
+// OCP E4M3 code (FP8 pools): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits.
+struct fp8_t {
+  uint8_t bits;
+};
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -35,6 +39,10 @@ struct Elem<f16_t> {
 template <>
 struct Elem<bf16_t> {
   static constexpr int kBytes = 2;
+};
+template <>
+struct Elem<fp8_t> {
+  static constexpr int kBytes = 1;
 };
 
 // Elements of T per 16-byte load.
@@ -59,6 +67,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+
+// float32 -> E4M3 code (in the low byte): nearest value, ties to the even
+// code, magnitudes from 448 up (infinity included) saturate to 448, NaN
+// stays NaN, the sign of zero is kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;   // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |x| >= 448
+  if (a < 0x3c800000u) {
+    // Below 2^-6 the codes are multiples of 2^-9 (subnormals); scaling by
+    // 2^9 is exact and v_rndne rounds half to even, giving 0..8 (8 is the
+    // smallest normal, code 0x08).
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  // Normal: keep 3 of the 23 mantissa bits, rounding the 20 dropped bits to
+  // nearest even; the carry may step into the exponent, which is still right.
+  // Rebias the exponent from 127 to 7.
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+// Two E4M3 codes held in bits 15:8 and 31:24 of x (other bits zero) -> an
+// f16x2 word whose halves equal the codes' values times 2^-8, exactly: the
+// sign stays in bit 15 and the 7 exponent+mantissa bits move down one place,
+// so the E4M3 exponent field (bias 7) becomes the low four bits of the f16
+// exponent field (bias 15) and subnormals stay subnormal.  Code 0x7f (NaN)
+// maps to a finite value; quantised pools never hold it.
+__device__ __forceinline__ uint32_t e4m3_pair_to_f16x2(uint32_t x) {
+  return (x & 0x80008000u) | ((x >> 1) & 0x3f803f80u);
+}
+
+// v_perm_b32 selectors that place two bytes of a word in bits 15:8 and
+// 31:24 (zeros elsewhere): bytes (0, 1) and (2, 3) of the second operand.
+constexpr uint32_t kPermBytes01 = 0x010c000cu;
+constexpr uint32_t kPermBytes23 = 0x030c020cu;
 
 // Unpack one 32-bit word holding two storage elements (or one f32) to floats.
 template <typename T>

@@ -8,13 +8,14 @@
 
 namespace pa {
 
-enum class DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum class DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
 struct KvCacheArgs {
   void* key_cache;
   void* value_cache;
   int32_t num_blocks, num_kv_heads, head_dim, block_size;
   DType dtype;
+  float k_scale, v_scale;  // FP8 pools: code c stands for value(c) * scale
 };
 
 struct DecodeArgs {

@@ -17,8 +17,12 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
-_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+# An FP8 (OCP E4M3) pool is a uint8 (or float8_e4m3fn) tensor of codes; its
+# queries, outputs and new K/V rows are float16.
+_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
+if hasattr(torch, "float8_e4m3fn"):
+    _DTYPE[torch.float8_e4m3fn] = PA_FP8_E4M3
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH",
            6: "PA_ERR_NO_BLOCKS", 7: "PA_ERR_NOT_FOUND", 8: "PA_ERR_EXISTS"}
 PA_ERR_NO_BLOCKS = 6
@@ -39,6 +43,8 @@ class pa_kv_cache(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -152,16 +158,31 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor) -> pa_kv_cache:
-    """Describe a pool of shape [num_blocks, num_kv_heads, block_size, head_dim]."""
+def is_fp8(key_cache: torch.Tensor) -> bool:
+    return _DTYPE.get(key_cache.dtype) == PA_FP8_E4M3
+
+
+def io_dtype(key_cache: torch.Tensor) -> torch.dtype:
+    """dtype of the queries, outputs and new K/V rows that go with a pool."""
+    return torch.float16 if is_fp8(key_cache) else key_cache.dtype
+
+
+def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor, scales=None) -> pa_kv_cache:
+    """Describe a pool of shape [num_blocks, num_kv_heads, block_size, head_dim].
+
+    ``scales`` = (k_scale, v_scale) is required for an FP8 pool: a code c
+    stands for value(c) * scale."""
     _need(key_cache, "key_cache")
     _need(value_cache, "value_cache", key_cache.dtype)
     if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
         raise ValueError("key_cache/value_cache must both be [num_blocks, num_kv_heads, block_size, head_dim]")
     if key_cache.dtype not in _DTYPE:
         raise ValueError(f"unsupported cache dtype {key_cache.dtype}")
+    if is_fp8(key_cache) and scales is None:
+        raise ValueError("an FP8 pool needs scales=(k_scale, v_scale)")
+    ks, vs = (1.0, 1.0) if scales is None else (float(scales[0]), float(scales[1]))
     NB, H, B, D = key_cache.shape
-    return pa_kv_cache(key_cache.data_ptr(), value_cache.data_ptr(), NB, H, D, B, _DTYPE[key_cache.dtype])
+    return pa_kv_cache(key_cache.data_ptr(), value_cache.data_ptr(), NB, H, D, B, _DTYPE[key_cache.dtype], ks, vs)
 
 
 def _check(status: int, what: str):
@@ -185,10 +206,10 @@ def pa_slot_mapping(block_tables, seq_lens, cu_q_lens, block_size: int, slot_map
     return slot_mapping
 
 
-def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, stream=None):
-    c = kv_cache(key_cache, value_cache)
-    _need(key, "key", key_cache.dtype)
-    _need(value, "value", key_cache.dtype)
+def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, stream=None, scales=None):
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(key, "key", io_dtype(key_cache))
+    _need(value, "value", io_dtype(key_cache))
     _need(slot_mapping, "slot_mapping", torch.int64)
     T = key.shape[0]
     if key.shape != (T, c.num_kv_heads, c.head_dim) or value.shape != key.shape or slot_mapping.shape[0] < T:
@@ -198,10 +219,10 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, strea
 
 
 def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len: int,
-                 slot_mapping=None, stream=None):
-    c = kv_cache(key_cache, value_cache)
-    _need(key, "key", key_cache.dtype)
-    _need(value, "value", key_cache.dtype)
+                 slot_mapping=None, stream=None, scales=None):
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(key, "key", io_dtype(key_cache))
+    _need(value, "value", io_dtype(key_cache))
     _need(block_tables, "block_tables", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(cu_q_lens, "cu_q_lens", torch.int32)
@@ -235,10 +256,10 @@ def decode_workspace(query, key_cache, max_seq_len: int, partition_size: int = 0
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
-              workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None):
-    c = kv_cache(key_cache, value_cache)
-    _need(query, "query", key_cache.dtype)
-    _need(out, "out", key_cache.dtype)
+              workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None, scales=None):
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
     _need(block_tables, "block_tables", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     S, Hq, D = query.shape
@@ -256,10 +277,10 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale:
 
 
 def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, block_tables, scale: float,
-                     max_q_len: int, stream=None):
-    c = kv_cache(key_cache, value_cache)
-    _need(query, "query", key_cache.dtype)
-    _need(out, "out", key_cache.dtype)
+                     max_q_len: int, stream=None, scales=None):
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
     _need(cu_q_lens, "cu_q_lens", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(block_tables, "block_tables", torch.int32)
@@ -276,7 +297,7 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, bl
 
 def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
     """Pool block src[i] -> pool block dst[i] (device int32 tensors)."""
-    c = kv_cache(key_cache, value_cache)
+    c = kv_cache(key_cache, value_cache, (1.0, 1.0))  # bit copies: scales unused
     _need(src, "src", torch.int32)
     _need(dst, "dst", torch.int32)
     if src.shape != dst.shape:
@@ -292,7 +313,7 @@ def _buf_ok(t, key_cache, n, name):
 
 
 def pa_gather_blocks(key_cache, value_cache, block_ids, key_out, value_out, stream=None):
-    c = kv_cache(key_cache, value_cache)
+    c = kv_cache(key_cache, value_cache, (1.0, 1.0))  # bit copies: scales unused
     _need(block_ids, "block_ids", torch.int32)
     n = block_ids.numel()
     _buf_ok(key_out, key_cache, n, "key_out")
@@ -302,7 +323,7 @@ def pa_gather_blocks(key_cache, value_cache, block_ids, key_out, value_out, stre
 
 
 def pa_scatter_blocks(key_cache, value_cache, block_ids, key_in, value_in, stream=None):
-    c = kv_cache(key_cache, value_cache)
+    c = kv_cache(key_cache, value_cache, (1.0, 1.0))  # bit copies: scales unused
     _need(block_ids, "block_ids", torch.int32)
     n = block_ids.numel()
     _buf_ok(key_in, key_cache, n, "key_in")

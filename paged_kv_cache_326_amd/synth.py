@@ -292,31 +292,43 @@ CONFIG_NAMES = {
 }
 
 
-def config(k: int, *, poison_unused: bool = True, scale_down: int = 1) -> Workload:
+def config(k: int, *, poison_unused: bool = True, scale_down: int = 1, dtype: Optional[str] = None) -> Workload:
     """Workload for config ``k`` (1..5).
 
     ``scale_down`` > 1 shrinks sequence lengths (and the pool with them) by
     that factor, keeping heads, head_dim, block size, dtype and the length
     mix; it exists so that full-comparison parity runs stay small.
+    ``dtype`` replaces the config's storage dtype (same draws, rounded to the
+    other type): FP8 pools are filled from float16 rows.
     """
+    return _config(k, poison_unused=poison_unused, scale_down=scale_down, dtype=dtype)
+
+
+def _config(k: int, *, poison_unused: bool, scale_down: int, dtype: Optional[str]) -> Workload:
     rng = np.random.default_rng(326000 + k)
     sd = int(scale_down)
+
+    def make(**kw):
+        if dtype is not None:
+            kw["dtype"] = dtype
+        return build(**kw)
+
     if k == 1:
-        return build(
+        return make(
             name=CONFIG_NAMES[1], seed=0, rng=rng, dtype="f32", num_heads=8, num_kv_heads=2,
             head_dim=64, block_size=16, seq_lens=[5, 17, 33, 50], num_blocks=64,
             poison_unused=poison_unused,
         )
     if k == 2:
         L = max(4096 // sd, 1)
-        return build(
+        return make(
             name=CONFIG_NAMES[2], seed=0, rng=rng, dtype="f16", num_heads=64, num_kv_heads=8,
             head_dim=128, block_size=16, seq_lens=[L] * 16, poison_unused=poison_unused,
         )
     if k == 3:
         lens = np.exp(rng.uniform(math.log(50), math.log(8000), size=64))
         lens = np.maximum(np.rint(lens / sd).astype(np.int64), 1)
-        return build(
+        return make(
             name=CONFIG_NAMES[3], seed=0, rng=rng, dtype="bf16", num_heads=32, num_kv_heads=8,
             head_dim=128, block_size=16, seq_lens=lens, pool_factor=1.2,
             poison_unused=poison_unused,
@@ -325,7 +337,7 @@ def config(k: int, *, poison_unused: bool = True, scale_down: int = 1) -> Worklo
         prefix = max(1024 // sd // 16, 1) * 16
         private = max(256 // sd, 1)
         groups = np.repeat(np.arange(8), 4)
-        return build(
+        return make(
             name=CONFIG_NAMES[4], seed=0, rng=rng, dtype="f16", num_heads=32, num_kv_heads=8,
             head_dim=128, block_size=16, seq_lens=[prefix + private] * 32,
             shared_prefix=groups, prefix_len=prefix, poison_unused=poison_unused,
@@ -336,7 +348,7 @@ def config(k: int, *, poison_unused: bool = True, scale_down: int = 1) -> Worklo
         dec = max(2048 // sd, 1)
         lens = [ctx + chunk] * 4 + [dec] * 48
         qls = [chunk] * 4 + [1] * 48
-        return build(
+        return make(
             name=CONFIG_NAMES[5], seed=0, rng=rng, dtype="bf16", num_heads=64, num_kv_heads=8,
             head_dim=128, block_size=32, seq_lens=lens, q_lens=qls, poison_unused=poison_unused,
         )
