@@ -265,6 +265,36 @@ pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, 
  *                       length (blocks), -1 if unknown
  * pa_bm_free_list       copies up to capacity free ids in pool order;
  *                       returns the number of free blocks
+ *
+ * Prefix cache.  [P1] "工程边界与架构取舍": requests sharing a system prompt
+ * reuse the prefix's physical blocks; cached prefixes are marked by hash and
+ * carry a version, and a hash collision must not produce a wrong hit.
+ * A full block is cached once pa_bm_commit reports its K/V written; its key
+ * is (version, the exact token prefix it ends).  Lookups go through a
+ * chained 64-bit hash (parent hash, version, the block's token ids) and
+ * accept a candidate only if version, parent block and token ids match.
+ * Every cached block's parent is cached; a cached block whose references
+ * are all released stays cached in the free list until a fresh allocation
+ * pops it, which uncaches it and every cached block extending it.
+ *
+ * pa_bm_add_sequence_tokens  new sequence with token ids; its leading full
+ *                       blocks that are cached for this version are shared
+ *                       (taken back from the free list if needed) and
+ *                       *num_cached_tokens = their tokens (the caller skips
+ *                       their K/V); the rest are fresh.  All or nothing.
+ * pa_bm_append_token_ids  pa_bm_append_tokens with the new tokens' ids
+ *                       (PA_ERR_SHAPE if the sequence's ids are not known;
+ *                       pa_bm_append_tokens forgets them)
+ * pa_bm_commit          the first num_computed_tokens tokens' K/V are in
+ *                       the pool: cache their full blocks, in order,
+ *                       stopping at a block whose parent is not cached or
+ *                       whose key another block already holds
+ * pa_bm_drop_version    uncache every block of a version (a changed system
+ *                       prompt); returns how many
+ * pa_bm_cached_blocks   number of cached blocks; pa_bm_is_cached: 1 / 0
+ * pa_bm_set_hash_bits   keep only the low bits of the hash (1..64, default
+ *                       64; only while nothing is cached): forces collisions
+ *                       so the exact-match check can be exercised
  */
 typedef struct pa_block_manager pa_block_manager;
 pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
@@ -279,6 +309,15 @@ pa_status pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
 int32_t pa_bm_block_table(pa_block_manager* bm, int64_t seq_id, int32_t* out, int32_t capacity);
 int64_t pa_bm_num_tokens(pa_block_manager* bm, int64_t seq_id);
 int32_t pa_bm_free_list(pa_block_manager* bm, int32_t* out, int32_t capacity);
+pa_status pa_bm_add_sequence_tokens(pa_block_manager* bm, int64_t seq_id, const int32_t* token_ids,
+                                    int32_t num_tokens, uint64_t version, int32_t* num_cached_tokens);
+pa_status pa_bm_append_token_ids(pa_block_manager* bm, int64_t seq_id, const int32_t* token_ids, int32_t num_new,
+                                 int32_t* copy_src, int32_t* copy_dst, int32_t* num_copies);
+pa_status pa_bm_commit(pa_block_manager* bm, int64_t seq_id, int32_t num_computed_tokens);
+int32_t pa_bm_drop_version(pa_block_manager* bm, uint64_t version);
+int32_t pa_bm_cached_blocks(pa_block_manager* bm);
+int32_t pa_bm_is_cached(pa_block_manager* bm, int32_t block);
+pa_status pa_bm_set_hash_bits(pa_block_manager* bm, int32_t bits);
 
 const char* pa_status_string(pa_status status);
 const char* pa_version(void);

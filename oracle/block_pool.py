@@ -10,9 +10,22 @@ Sources:
   [P2] "KV Cache管理优化：大模型推理显存瓶颈突破", section 2.1 (the same
        FIFO allocator) and section 4.1 (a shared block counts its users and
        goes back to the pool when the count reaches zero).
+  [P1] section "工程边界与架构取舍": requests that share a system prompt can
+       reuse the prefix's physical blocks; cached prefixes carry a version
+       (an updated prompt must not hit the old cache), and a hash collision
+       must never produce a wrong hit.
 Where the pages are silent the model takes these readings: a failed request
 changes nothing; a sequence about to write into a partly filled block that
 other sequences share first receives a private copy (copy-on-write).
+
+Prefix cache (readings): a full block becomes cached when the caller
+reports its K/V written (commit); its key is the version plus the exact
+token prefix the block ends.  A new sequence reuses the cached blocks of its
+longest cached run of leading full blocks.  A cached block stays cached
+after its last reference goes (it sits in the free list) until a fresh
+allocation pops it, which uncaches it together with every cached key that
+extends it.  The model keys its dict by the full token tuple, so no hash is
+involved at all: the library's hashed lookup must behave exactly like it.
 """
 
 from collections import deque
@@ -33,11 +46,30 @@ class BlockPoolModel:
         self.refs = [0] * num_blocks
         self.tables = {}
         self.lengths = {}
+        self.ids = {}        # sequence -> token ids (None when not all known)
+        self.version = {}    # sequence -> version
+        self.cached = {}     # (version, token prefix tuple) -> block
+        self.key_of = {}     # block -> its key
+
+    def _uncache(self, b):
+        version, prefix = self.key_of.pop(b)
+        del self.cached[(version, prefix)]
+        n = len(prefix)
+        for (v2, p2), b2 in list(self.cached.items()):
+            if v2 == version and len(p2) > n and p2[:n] == prefix and b2 in self.key_of:
+                self._uncache(b2)
 
     def _take(self):
         b = self.free.popleft()
+        if b in self.key_of:
+            self._uncache(b)
         self.refs[b] = 1
         return b
+
+    def _ref(self, b):
+        if self.refs[b] == 0:
+            self.free.remove(b)
+        self.refs[b] += 1
 
     def _release(self, b):
         self.refs[b] -= 1
@@ -51,15 +83,61 @@ class BlockPoolModel:
             raise NoBlocks
         self.tables[sid] = [self._take() for _ in range(need)]
         self.lengths[sid] = n
+        self.ids[sid] = None
+        self.version[sid] = 0
+
+    def add_sequence_tokens(self, sid, ids, version=0):
+        """Returns how many leading tokens were found cached."""
+        assert sid not in self.tables
+        ids, B = [int(x) for x in ids], self.block_size
+        hits = []
+        for i in range(len(ids) // B):
+            b = self.cached.get((version, tuple(ids[: (i + 1) * B])))
+            if b is None:
+                break
+            hits.append(b)
+        need = blocks_needed(len(ids), B) - len(hits)
+        if need > len(self.free) - sum(1 for b in hits if self.refs[b] == 0):
+            raise NoBlocks
+        for b in hits:
+            self._ref(b)
+        self.tables[sid] = hits + [self._take() for _ in range(need)]
+        self.lengths[sid] = len(ids)
+        self.ids[sid] = ids
+        self.version[sid] = version
+        return len(hits) * B
+
+    def commit(self, sid, n):
+        """The first n tokens' K/V are written: cache the full blocks among them."""
+        t, ids, B, v = self.tables[sid], self.ids[sid], self.block_size, self.version[sid]
+        for i in range(n // B):
+            if t[i] in self.key_of:
+                continue
+            if i > 0 and t[i - 1] not in self.key_of:
+                break
+            key = (v, tuple(ids[: (i + 1) * B]))
+            if key in self.cached:
+                break
+            self.cached[key] = t[i]
+            self.key_of[t[i]] = key
+
+    def drop_version(self, version):
+        gone = [b for b, (v, _) in self.key_of.items() if v == version]
+        for b in gone:
+            if b in self.key_of:
+                self._uncache(b)
+        return len(gone)
 
     def fork(self, parent, child):
         assert child not in self.tables
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
+        self.ids[child] = None if self.ids[parent] is None else list(self.ids[parent])
+        self.version[child] = self.version[parent]
         for b in self.tables[child]:
             self.refs[b] += 1
 
-    def append_tokens(self, sid, n):
+    def append_tokens(self, sid, n, ids=None):
         """Returns the copy-on-write (old, new) pairs."""
         if n == 0:
             return []
@@ -77,12 +155,16 @@ class BlockPoolModel:
             pairs.append((old, new))
         t.extend(self._take() for _ in range(grow))
         self.lengths[sid] = L + n
+        if ids is None or self.ids[sid] is None:
+            self.ids[sid] = None
+        else:
+            self.ids[sid].extend(int(x) for x in ids)
         return pairs
 
     def free_sequence(self, sid):
         for b in self.tables.pop(sid):
             self._release(b)
-        del self.lengths[sid]
+        del self.lengths[sid], self.ids[sid], self.version[sid]
 
 
 def copy_blocks(pool, src, dst):

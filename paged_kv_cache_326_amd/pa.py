@@ -73,6 +73,13 @@ EXPORTS = (
     "pa_bm_block_table",
     "pa_bm_num_tokens",
     "pa_bm_free_list",
+    "pa_bm_add_sequence_tokens",
+    "pa_bm_append_token_ids",
+    "pa_bm_commit",
+    "pa_bm_drop_version",
+    "pa_bm_cached_blocks",
+    "pa_bm_is_cached",
+    "pa_bm_set_hash_bits",
     "pa_status_string",
     "pa_version",
 )
@@ -136,6 +143,21 @@ def lib() -> ctypes.CDLL:
     L.pa_bm_num_tokens.restype = i64
     L.pa_bm_free_list.argtypes = [bm, vp, i32]
     L.pa_bm_free_list.restype = i32
+    u64 = ctypes.c_uint64
+    L.pa_bm_add_sequence_tokens.argtypes = [bm, i64, vp, i32, u64, vp]
+    L.pa_bm_add_sequence_tokens.restype = ctypes.c_int
+    L.pa_bm_append_token_ids.argtypes = [bm, i64, vp, i32, vp, vp, vp]
+    L.pa_bm_append_token_ids.restype = ctypes.c_int
+    L.pa_bm_commit.argtypes = [bm, i64, i32]
+    L.pa_bm_commit.restype = ctypes.c_int
+    L.pa_bm_drop_version.argtypes = [bm, u64]
+    L.pa_bm_drop_version.restype = i32
+    L.pa_bm_cached_blocks.argtypes = [bm]
+    L.pa_bm_cached_blocks.restype = i32
+    L.pa_bm_is_cached.argtypes = [bm, i32]
+    L.pa_bm_is_cached.restype = i32
+    L.pa_bm_set_hash_bits.argtypes = [bm, i32]
+    L.pa_bm_set_hash_bits.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -333,7 +355,7 @@ def pa_scatter_blocks(key_cache, value_cache, block_ids, key_in, value_in, strea
 
 
 class BlockManager:
-    """The library's host-side block manager (FIFO pool, refcounts, copy-on-write)."""
+    """The library's host-side block manager (FIFO pool, refcounts, copy-on-write, prefix cache)."""
 
     def __init__(self, num_blocks: int, block_size: int, free_order=None):
         L = lib()
@@ -397,6 +419,42 @@ class BlockManager:
         buf = (ctypes.c_int32 * max(n, 1))()
         L.pa_bm_free_list(self._h, buf, n)
         return list(buf[:n])
+
+    # Prefix cache
+    @staticmethod
+    def _ids(token_ids):
+        arr = (ctypes.c_int32 * max(len(token_ids), 1))(*[int(x) for x in token_ids])
+        return arr, len(token_ids)
+
+    def add_sequence_tokens(self, seq_id: int, token_ids, version: int = 0) -> int:
+        """New sequence with token ids; returns how many leading tokens were found cached."""
+        arr, n = self._ids(token_ids)
+        hit = ctypes.c_int32()
+        _check(lib().pa_bm_add_sequence_tokens(self._h, int(seq_id), arr, n, int(version), ctypes.addressof(hit)),
+               "pa_bm_add_sequence_tokens")
+        return hit.value
+
+    def append_token_ids(self, seq_id: int, token_ids):
+        arr, n = self._ids(token_ids)
+        src, dst, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_bm_append_token_ids(self._h, int(seq_id), arr, n, ctypes.addressof(src), ctypes.addressof(dst),
+                                            ctypes.addressof(k)), "pa_bm_append_token_ids")
+        return [(src.value, dst.value)] if k.value else []
+
+    def commit(self, seq_id: int, num_computed_tokens: int):
+        _check(lib().pa_bm_commit(self._h, int(seq_id), int(num_computed_tokens)), "pa_bm_commit")
+
+    def drop_version(self, version: int) -> int:
+        return int(lib().pa_bm_drop_version(self._h, int(version)))
+
+    def cached_blocks(self) -> int:
+        return int(lib().pa_bm_cached_blocks(self._h))
+
+    def is_cached(self, block: int) -> bool:
+        return lib().pa_bm_is_cached(self._h, int(block)) == 1
+
+    def set_hash_bits(self, bits: int):
+        _check(lib().pa_bm_set_hash_bits(self._h, int(bits)), "pa_bm_set_hash_bits")
 
 
 def version() -> str:
