@@ -82,7 +82,12 @@ typedef enum {
 } pa_status;
 
 /* One layer's paged KV pool.  Both arrays are device memory owned by the
- * caller, shape [num_blocks][num_kv_heads][block_size][head_dim], `dtype`.
+ * caller, in `dtype`: key_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ * and value_cache [num_blocks][num_kv_heads][head_dim][block_size].  Every
+ * (block, KV head) tile is contiguous ([P1] "PagedAttention 的 CUDA Kernel
+ * 实现": a block's vectors are adjacent so its reads coalesce); value tiles
+ * are stored transposed so that the tokens of one dimension are adjacent,
+ * which makes both attention products contiguous matrix-core operand loads.
  * k_scale and v_scale are read only for PA_FP8_E4M3 (must then be positive
  * and finite, else PA_ERR_SHAPE): a key code c stands for value(c) * k_scale,
  * a value code for value(c) * v_scale.  New rows are quantised as
@@ -119,7 +124,8 @@ pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_se
                           int64_t* slot_mapping, int32_t num_tokens,
                           hipStream_t stream);
 
-/* Scatter new tokens' K and V into their pool slots (bit-exact copy).
+/* Scatter new tokens' K and V into their pool slots (bit-exact copy; a
+ * token's value row becomes column `offset` of its block's value tile).
  * [P1] "KV Cache 的内存开销与分页机制": the new token's vectors are stored in
  * the current block, or in a block appended to the table when it is full.
  *
@@ -169,9 +175,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *
  * out, query    [num_seqs][num_heads][head_dim], cache->dtype, float16 for
  *               an FP8 pool (out is rounded from float32 to nearest-even).
- *               An FP8 pool needs head_dim 128 (else PA_ERR_UNSUPPORTED); its
- *               codes are widened exactly to float16 in registers and the
- *               scales applied to the float32 logits and outputs.
+ *               An FP8 pool's codes are widened exactly to float16 in
+ *               registers and its scales applied to the float32 logits and
+ *               outputs.
  * max_seq_len   host-side upper bound of seq_lens (<= max_blocks_per_seq *
  *               block_size); longer device values are clamped to it
  * workspace     device scratch of at least pa_decode_workspace_bytes(); may
@@ -229,8 +235,9 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* quer
  *                    must not be any src of the same call)
  * pa_gather_blocks   pool block block_ids[i] -> row i of key_out/value_out
  * pa_scatter_blocks  row i of key_in/value_in -> pool block block_ids[i]
- * Buffers are [num_blocks][num_kv_heads][block_size][head_dim] in the cache
- * dtype, device memory or pinned host memory (hipHostMalloc), so a gather or
+ * Buffers are laid out like the pool's blocks (key: [n][num_kv_heads]
+ * [block_size][head_dim], value: [n][num_kv_heads][head_dim][block_size]) in
+ * the cache dtype, device memory or pinned host memory (hipHostMalloc), so a gather or
  * scatter through a pinned buffer swaps blocks out of or into HBM; other
  * host memory is refused with PA_ERR_UNSUPPORTED.  Ids outside
  * [0, cache->num_blocks) are skipped.

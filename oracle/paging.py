@@ -70,9 +70,11 @@ def reshape_and_cache(
 ) -> None:
     """Write each new token's K and V (all KV heads) into its pool slot, in place.
 
-    Cache layout [num_blocks, num_kv_heads, block_size, head_dim]: within one
-    (block, KV head) the block's token vectors are contiguous, the layout that
-    lets in-block KV reads coalesce ([P1] "PagedAttention 的 CUDA Kernel 实现").
+    Pool layouts: keys [num_blocks, num_kv_heads, block_size, head_dim],
+    values [num_blocks, num_kv_heads, head_dim, block_size].  Each (block, KV
+    head) tile is one contiguous piece of memory, the property that lets
+    in-block KV reads coalesce ([P1] "PagedAttention 的 CUDA Kernel 实现");
+    inside a value tile a dimension's block_size values are adjacent.
     A negative slot marks a padding token and is skipped; two tokens may not
     share a slot.  Values are copied bit for bit.
     """
@@ -86,7 +88,7 @@ def reshape_and_cache(
             continue
         block, offset = int(slot) // B, int(slot) % B
         key_cache[block, :, offset, :] = key[t]
-        value_cache[block, :, offset, :] = value[t]
+        value_cache[block, :, :, offset] = value[t]
 
 
 def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndarray, seq_len: int):
@@ -100,7 +102,8 @@ def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndar
     B = key_cache.shape[2]
     n = blocks_needed(seq_len, B)
     phys = np.asarray(table_row[:n], dtype=np.int64)
-    # [n, Hkv, B, D] -> [n, B, Hkv, D] -> [n*B, Hkv, D]; logical order is block-major, offset-minor.
+    # Logical order is block-major, offset-minor:
+    # keys [n, Hkv, B, D] -> [n, B, Hkv, D]; values [n, Hkv, D, B] -> [n, B, Hkv, D].
     K = key_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, key_cache.shape[1], key_cache.shape[3])
-    V = value_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, value_cache.shape[1], value_cache.shape[3])
+    V = value_cache[phys].transpose(0, 3, 1, 2).reshape(n * B, value_cache.shape[1], value_cache.shape[2])
     return K[:seq_len], V[:seq_len]

@@ -170,7 +170,7 @@ pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, 
 }
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {
-  // Aim for at least two (8-wave) workgroups per compute unit; longer
+  // Aim for at least two (4-wave) workgroups per compute unit; longer
   // partitions amortise each workgroup's start-up and the merge, shorter
   // ones fill the chip when there are few (sequence, KV head) pairs.
   if (block_size <= 0) return 0;
@@ -200,7 +200,6 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, c
   if (!supported_group(num_heads, cache->num_kv_heads)) {
     return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
   }
-  if (cache->dtype == PA_FP8_E4M3 && cache->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
   int p = partition_size;
   if (p == 0) p = pa_decode_auto_partition(num_seqs, cache->num_kv_heads, max_seq_len, cache->block_size);

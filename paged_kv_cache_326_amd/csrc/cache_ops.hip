@@ -69,10 +69,52 @@ __device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4& data
   *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
 }
 
+// Store the same chunk as one column piece of a transposed value tile:
+// element e goes to p[e * stride].
+template <typename T>
+__device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4& data, float scale) {
+  if constexpr (Elem<T>::kBytes == 4) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e * stride] = data[e];
+  } else if constexpr (Elem<T>::kBytes == 2) {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t word = data[e / 2];
+      q[e * stride] = (uint16_t)(word >> (16 * (e % 2)));
+    }
+  } else {
+    uint8_t* q = reinterpret_cast<uint8_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t word = data[e / 2];
+      const float x = e % 2 ? f16_hi(word) : f16_lo(word);
+      q[e * stride] = (uint8_t)f32_to_e4m3(x / scale);
+    }
+  }
+}
+
+// The destination of one 16-byte source chunk (dims ch*VEC ..) of token
+// slot (blk, off), KV head h: a key row piece, or a value column piece.
+template <typename T>
+__device__ __forceinline__ void store_kv_chunk(T* key_cache, T* value_cache, int which, int64_t blk, int off, int h,
+                                               int ch, int vec, int num_kv_heads, int head_dim, int block_size,
+                                               const u32x4& data, float k_scale, float v_scale) {
+  if (which == 0) {
+    T* dst = key_cache + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * vec;
+    store_chunk<T>(dst, data, k_scale);
+  } else {
+    T* dst = value_cache + ((blk * num_kv_heads + h) * head_dim + ch * vec) * block_size + off;
+    store_column<T>(dst, block_size, data, v_scale);
+  }
+}
+
 // Each thread moves one 16-byte chunk of one token's K or V row.  A token row
-// of one KV head is head_dim elements; the pool tile of (block, KV head) is
-// [block_size][head_dim], so the destination of (token, head) is
-//   ((block * num_kv_heads + head) * block_size + offset) * head_dim.
+// of one KV head is head_dim elements.  The key tile of (block, KV head) is
+// [block_size][head_dim] (the row lands at
+//   ((block * num_kv_heads + head) * block_size + offset) * head_dim),
+// the value tile [head_dim][block_size] (the row becomes column `offset`).
 template <typename T>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
     T* __restrict__ key_cache, T* __restrict__ value_cache, const typename Src<T>::type* __restrict__ key,
@@ -96,9 +138,8 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
   const int64_t blk = slot / block_size;
   const int off = (int)(slot % block_size);
   const S* src = (which ? value : key) + ((int64_t)t * num_kv_heads + h) * head_dim + ch * VEC;
-  T* dst = (which ? value_cache : key_cache) +
-           ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
-  store_chunk<T>(dst, *reinterpret_cast<const u32x4*>(src), which ? v_scale : k_scale);
+  store_kv_chunk<T>(key_cache, value_cache, which, blk, off, h, ch, VEC, num_kv_heads, head_dim, block_size,
+                    *reinterpret_cast<const u32x4*>(src), k_scale, v_scale);
 }
 
 // Slot mapping and scatter in one pass.  Workgroup (x, s) covers new tokens
@@ -145,8 +186,8 @@ __global__ void __launch_bounds__(256) append_kernel(
     if (slot < 0 || phys >= num_blocks) continue;
     const int64_t blk = slot / block_size;
     const int off = (int)(slot % block_size);
-    T* dst = (which ? value_cache : key_cache) + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * VEC;
-    store_chunk<T>(dst, data, which ? v_scale : k_scale);
+    store_kv_chunk<T>(key_cache, value_cache, which, blk, off, h, ch, VEC, num_kv_heads, head_dim, block_size, data,
+                      k_scale, v_scale);
   }
 }
 

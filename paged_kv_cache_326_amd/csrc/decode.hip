@@ -1,33 +1,49 @@
-// Paged decode attention for gfx950 (MI355X).
+// Paged decode attention for gfx950 (MI355X) on the matrix cores.
 //
 // Sources: [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践",
 // sections "PagedAttention 的 CUDA Kernel 实现" (look up each logical block's
 // physical ID in the block table, then read the block's contiguous K/V; the
-// table sits on chip; in-block reads coalesce) and "工程边界与架构取舍"
-// (decode is bound by reading the whole KV cache for one token).
+// table sits on chip; in-block reads coalesce; the next block is fetched
+// while the current one is used) and "工程边界与架构取舍" (decode is bound by
+// reading the whole KV cache for one token).
 //
-// Work decomposition.  One workgroup of NW (8) wavefronts handles one
+// Work decomposition.  One workgroup of kNW wavefronts handles one
 // (partition, KV head, sequence): a partition is `partition` consecutive
 // tokens of the sequence (a multiple of the block size).  All G query heads
-// that share the KV head are served by the same workgroup, so every K/V block
-// is read from HBM once per KV head.
+// that share the KV head are served together, so every K/V byte is read from
+// HBM once.  The partition is cut into steps of 32 tokens; wave w takes steps
+// w, w + kNW, ... and keeps the next steps' K/V loads in flight (a register
+// ring) while it computes the current one.
 //
-//   1. The partition's block-table entries are staged in LDS.
-//   2. QK: each wave takes blocks w, w+NW, ...  A token's K row is split over
-//      8 lanes (16-byte loads, 128 contiguous bytes per 8 lanes), every lane
-//      dots its slice with the G query heads (v_dot2 for f16/bf16), and a
-//      3-step DPP reduce-scatter over the 8 lanes leaves each lane with the
-//      full logit of one head.  Logits, pre-multiplied by scale*log2(e), go
-//      to LDS as [token][head].
-//   3. Softmax: per-head maximum over the partition, p = 2^(z - max) written
-//      back in place, per-head sums.
-//   4. PV: a token's V row is split over D/VEC lanes (16 bytes each), each
-//      lane accumulates p * v for all G heads in fp32; lanes holding the same
-//      dims are summed with cross-lane moves, waves through LDS.
-//   5. A sequence that fits one partition is normalised and written directly.
-//      Longer sequences write (max, sum, unnormalised o) per partition to the
-//      workspace and a second kernel merges them:
-//        M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Per step, with the G heads as the 16-wide N side of v_mfma_f32_16x16x*
+// (heads G..15 are zero columns):
+//   S[token][head]    = K . Q^T     two 16-token halves; K rows are plain
+//                                   16-byte loads of the key tile
+//   online softmax per head (running max and sum per lane, rescale of the
+//   accumulators when the max grows)
+//   O^T[dim][head]   += V^T . P^T   V^T comes straight from the transposed
+//                                   value tile (8 tokens of one dimension per
+//                                   lane), P^T straight from the lane's own
+//                                   logits
+// The 16 K rows of the first half are tokens 8(r/4) + r%4 and of the second
+// half 8(r/4) + 4 + r%4 (r = row): the logits that land in lane (head r,
+// group g) are then exactly tokens 8g .. 8g+7 of the step, which is the
+// k-slice the same lane holds in the PV product, and the one its value load
+// fetches; nothing moves between lanes except the per-head maximum.
+//
+// Operand layouts (lane l, r = l % 16, g = l / 16, j = 0..3):
+//   16x16x32 f16/bf16: A[m][k] m = r, k = 8g + e (e < 8); B[k][n] k = 8g + e, n = r
+//   16x16x4 f32:       A[m][k] m = r, k = g;             B[k][n] k = g, n = r
+//   C[m][n]: m = 4g + j, n = r
+// FP8 codes are widened exactly to f16 (value * 2^-8) on the way into the
+// f16 products; bf16 probabilities enter the PV product as a bf16 hi + lo
+// pair (two products), f16 ones rounded to f16 with the normaliser summing
+// the same rounded values.
+//
+// A sequence that fits one partition is normalised and written directly.
+// Longer sequences write (max, sum, unnormalised o) per partition to the
+// workspace and a second kernel merges them:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 #include <math.h>
 
 #include <type_traits>
@@ -39,209 +55,82 @@ namespace pa {
 
 namespace {
 
-constexpr int kNW = 8;  // wavefronts per workgroup (two workgroups per CU at 4 waves per SIMD)
+constexpr int kNW = 4;     // wavefronts per workgroup (two workgroups per CU at 2 waves per SIMD)
+constexpr int kStep = 32;  // tokens per step
 
-template <int G>
-struct Log2 {
-  static constexpr int v = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-};
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Dot product of two 16-byte chunks (8 x f16 / 8 x bf16 / 4 x f32) into fp32.
+// Per storage type: CE elements per 16-byte K load, KE k-elements per lane
+// per product, VW 32-bit words of V^T per lane per 16-dim tile and step (8
+// tokens), NBUF steps in the register ring.
 template <typename T>
-__device__ __forceinline__ float dot16(const u32x4& q, const u32x4& k, float acc);
-
+struct Dec;
 template <>
-__device__ __forceinline__ float dot16<f16_t>(const u32x4& q, const u32x4& k, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // Copy the lane out of the vector first: bit-casting a vector element
-    // lvalue in place reads the vector's first element.
-    const uint32_t qi = q[i], ki = k[i];
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qi), __builtin_bit_cast(f16x2, ki), acc, false);
-  }
-  return acc;
-}
-
-template <>
-__device__ __forceinline__ float dot16<bf16_t>(const u32x4& q, const u32x4& k, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t qi = q[i], ki = k[i];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(i16x2, qi), __builtin_bit_cast(i16x2, ki), acc, false);
-  }
-  return acc;
-}
-
-template <>
-__device__ __forceinline__ float dot16<float>(const u32x4& q, const u32x4& k, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), acc);
-  return acc;
-}
-
-// Query/output type of a pool dtype: FP8 pools take float16 queries.
-template <typename T>
-struct QType {
-  using type = T;
+struct Dec<f16_t> {
+  typedef f16_t Q;
+  static constexpr int CE = 8, KE = 8, VW = 4, NBUF = 2;
 };
 template <>
-struct QType<fp8_t> {
-  using type = f16_t;
-};
-
-// A 16-byte K chunk as dot-product operands in the query type: itself, or
-// for FP8 its 16 codes widened to two chunks of f16 pairs (values * 2^-8,
-// exact; the 2^8 goes into the logit scale).
-template <typename T>
-struct KOps {
-  static constexpr int kW = 1;
-  __device__ static __forceinline__ void widen(const u32x4& k, u32x4* out) { out[0] = k; }
+struct Dec<bf16_t> {
+  typedef bf16_t Q;
+  static constexpr int CE = 8, KE = 8, VW = 4, NBUF = 2;
 };
 template <>
-struct KOps<fp8_t> {
-  static constexpr int kW = 2;
-  __device__ static __forceinline__ void widen(const u32x4& k, u32x4* out) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = k[i];
-      out[i / 2][2 * (i % 2)] = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes01));
-      out[i / 2][2 * (i % 2) + 1] = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes23));
-    }
-  }
-};
-
-// V chunk one PV lane loads per token: 16 bytes, or 8 for FP8 (8 dims, so
-// that the lane's accumulators stay G * 8).
-template <typename T>
-struct VOps {
-  typedef u32x4 load_t;
-  static constexpr int kDims = vec16<T>();
+struct Dec<float> {
+  typedef float Q;
+  static constexpr int CE = 4, KE = 1, VW = 8, NBUF = 1;
 };
 template <>
-struct VOps<fp8_t> {
-  typedef u32x2 load_t;
-  static constexpr int kDims = 8;
+struct Dec<fp8_t> {
+  typedef f16_t Q;
+  static constexpr int CE = 16, KE = 8, VW = 2, NBUF = 2;
 };
 
-// 16 bytes of storage -> VEC floats.
-template <typename T>
-__device__ __forceinline__ void unpack16(const u32x4& v, float* f);
-
-template <>
-__device__ __forceinline__ void unpack16<f16_t>(const u32x4& v, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) unpack2<f16_t>(v[i], f[2 * i], f[2 * i + 1]);
+__device__ __forceinline__ f32x4 mma_f16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
-template <>
-__device__ __forceinline__ void unpack16<bf16_t>(const u32x4& v, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) unpack2<bf16_t>(v[i], f[2 * i], f[2 * i + 1]);
+__device__ __forceinline__ f32x4 mma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                 0);
 }
-template <>
-__device__ __forceinline__ void unpack16<float>(const u32x4& v, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One butterfly step of the 8-lane reduce-scatter.  N values per lane; the
-// partner lane differs in the bit selected by `hi`.  The lane keeps the upper
-// half of its values when `hi` is set, sends the other half, and adds what
-// the partner sent.  With N == 1 the step is a plain pairwise all-reduce.
-template <int N, int kCtrl>
-__device__ __forceinline__ void rs_step(float* a, bool hi) {
-  if constexpr (N > 1) {
-    constexpr int H = N / 2;
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const float send = hi ? a[j] : a[j + H];
-      const float keep = hi ? a[j + H] : a[j];
-      a[j] = keep + dpp_mov<kCtrl>(send);
-    }
-  } else {
-    a[0] += dpp_mov<kCtrl>(a[0]);
-  }
+// Four E4M3 codes (one word) -> two f16x2 words (values * 2^-8).
+__device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes01));
+  hi = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes23));
 }
 
-// Sum G per-lane partial logits over the 8 lanes of one token; afterwards lane
-// `sub` holds the full logit of head (sub >> (3 - log2 G)).
-template <int G>
-__device__ __forceinline__ float reduce_scatter8(float* a, int sub) {
-  rs_step<G, kDppHalfMirror>(a, (sub >> 2) & 1);
-  rs_step<(G >= 2 ? G / 2 : 1), kDppQuadXor2>(a, (sub >> 1) & 1);
-  rs_step<(G >= 4 ? G / 4 : 1), kDppQuadXor1>(a, sub & 1);
-  return a[0];
+// Two floats -> packed pair in the operand type, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
 
-// LDS layout of one workgroup.  Each wave owns one region that first holds
-// its logits/probabilities and, once its PV pass is done, its partial output
-// (only the owning wave ever touches its region, so the reuse needs no
-// barrier); f16 probability pairs, the per-wave (m, l), the block-table
-// slice and the query rows are separate.  At the benchmark shape the total
-// is ~27 KiB, so LDS never limits the four workgroups per CU that the VGPR
-// budget allows.
+// LDS of one workgroup: the partition's block-table slice, and per wave its
+// partial output [G][D], maximum and sum per head for the final merge.
 struct SmemLayout {
-  int bt_off, p_off, p_wave, h_off, h_wave, m_off, l_off, q_off, bytes;
+  int bt_off, o_off, m_off, l_off, bytes;
 };
 
 __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, int D) {
   SmemLayout s;
-  const int nblk = partition / B;
-  const int bpw = (nblk + kNW - 1) / kNW;  // blocks per wave
   int off = 0;
   s.bt_off = off;
-  off += (nblk * 4 + 15) & ~15;
-  s.p_off = off;
-  const int logits = bpw * B * G;  // floats
-  s.p_wave = logits > G * D ? logits : G * D;
-  off += kNW * s.p_wave * 4;
-  s.h_off = off;
-  s.h_wave = bpw * B / 2 * G;  // dwords per wave: f16 probability pairs
-  off += kNW * s.h_wave * 4;
+  off += ((partition / B) * 4 + 15) & ~15;
+  s.o_off = off;
+  off += kNW * G * D * 4;
   s.m_off = off;
   off += kNW * G * 4;
   s.l_off = off;
   off += kNW * G * 4;
-  s.q_off = off;  // the G query rows, as stored (at most 8 x 128 x 4 bytes)
-  off += G * D * 4;
   s.bytes = off;
   return s;
-}
-
-// Sum the per-lane PV accumulators x[NV] over the TS token slots of a wave
-// (the lanes that hold the same dims).  gfx950's row swaps do the first two
-// halvings: v_permlane32_swap exchanges the two 32-lane halves of a pair of
-// registers, v_permlane16_swap the odd rows of one with the even rows of the
-// other, so every swap-and-add halves the register count.  Afterwards lane
-// (row q, column c) holds full sums x[q * NV/R + j], j < NV/R, R = min(TS, 4),
-// rows counted in units of 64/R lanes; a third step (TS == 8) folds the two
-// slots that share a 16-lane row with a DPP rotate.
-template <int NV, int TS>
-__device__ __forceinline__ void reduce_slots(float* x) {
-  static_assert(TS == 2 || TS == 4 || TS == 8, "token slots");
-#pragma unroll
-  for (int j = 0; j < NV / 2; ++j) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j + NV / 2]), false, false);
-    x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  if constexpr (TS >= 4) {
-#pragma unroll
-    for (int j = 0; j < NV / 4; ++j) {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j + NV / 4]), false, false);
-      x[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-  }
-  if constexpr (TS == 8) {
-#pragma unroll
-    for (int j = 0; j < NV / 4; ++j) x[j] += dpp_mov<kDppRowRor8>(x[j]);
-  }
-}
-
-// Wave-local LDS ordering: the compiler may not move LDS accesses across this
-// point, and the wave's own earlier LDS writes are complete before later reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Combine the per-partition partials of one (sequence, query head, dim):
@@ -288,55 +177,38 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
   return den > 0.f ? num / den : 0.f;
 }
 
-template <typename T, int G>
-struct Occupancy {
-  // 1- and 2-byte types fit in 128 VGPRs (4 waves per SIMD); f32 is a
-  // correctness path and keeps the compiler's choice.
-  static constexpr int kWaves = Elem<T>::kBytes <= 2 ? 4 : 1;
-};
-
 template <typename T, int D, int B, int G>
-__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(Occupancy<T, G>::kWaves)))
+__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_partition_kernel(DecodeArgs a) {
-  using QT = typename QType<T>::type;
-  using VLoad = typename VOps<T>::load_t;
+  using QT = typename Dec<T>::Q;
   constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
-  constexpr int VEC = vec16<T>();   // K dims per 16-byte load
-  constexpr int QVEC = vec16<QT>(); // query elements per 16 bytes
-  constexpr int KW = KOps<T>::kW;   // operand chunks per K chunk
-  constexpr int LPT = 8;            // lanes per token (QK)
-  constexpr int DL = D / LPT;       // dims per lane (QK)
-  constexpr int NCK = DL / VEC;     // 16-byte chunks per lane per token (QK)
-  constexpr int CH = 16;            // tokens per pipeline stage (a chunk; B is 16 or 32)
-  constexpr int CPB = B / CH;       // chunks per block
-  constexpr int TPG = 64 / LPT;     // tokens per load group (QK)
-  constexpr int GPC = CH / TPG;     // load groups per chunk (QK)
-  constexpr int VV = VOps<T>::kDims; // dims per lane (PV)
-  constexpr int LPV = D / VV;       // lanes per token (PV)
-  constexpr int TS = 64 / LPV;      // token slots per load (PV)
-  constexpr int IPC = CH / TS;      // loads per chunk (PV)
+  constexpr bool kF32 = std::is_same<T, float>::value;
+  constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+  constexpr int CE = Dec<T>::CE, KE = Dec<T>::KE, VW = Dec<T>::VW, NBUF = Dec<T>::NBUF;
+  constexpr int NLK = D / (4 * CE);                 // K loads per lane per 16-token half
+  constexpr int NSUB = CE / KE;                     // products per K load
+  constexpr int QW = CE * (int)sizeof(QT) / 16;     // 16-byte query pieces per K load
+  constexpr int NDT = D / 16;                       // 16-dim tiles of the PV product
   constexpr int NT = kNW * 64;
-  constexpr int SHIFT = 3 - Log2<G>::v;
-  constexpr int NV = G * VV;        // PV accumulators per lane
-  static_assert(B % CH == 0 && NCK >= 1 && GPC >= 1 && IPC >= 1, "unsupported shape");
-  static_assert(64 % G == 0, "group size must divide the wave");
+  static_assert(NLK >= 1 && QW >= 1 && B % 8 == 0 && G <= 16, "unsupported shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // 1-D grid, (sequence, KV head) fastest and partition slowest.  Workgroup
-  // ids are dealt to the 8 XCDs round-robin, so this hands each XCD whole
-  // (sequence, KV head) pairs; with the partition fastest, XCD x would get
-  // partitions x and x+8 of everything and every short sequence's only
-  // partition would pile onto XCD 0.
+  // 1-D grid, (sequence, KV head) fastest and partition slowest: workgroup
+  // ids are dealt to the 8 XCDs round-robin, so each XCD gets whole
+  // (sequence, KV head) pairs and short sequences spread over all XCDs.
   const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
   const int part = blockIdx.x / (a.num_seqs * a.cache.num_kv_heads);
   const int g = sg % a.cache.num_kv_heads;
   const int s = sg / a.cache.num_kv_heads;
   const int P = a.partition;
+  const int nbp = P / B;
   const SmemLayout lay = smem_layout(P, B, G, D);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int r = lane & 15;   // MFMA row / column index of this lane
+  const int grp = lane >> 4; // MFMA k group of this lane
   const int Hkv = a.cache.num_kv_heads;
   const int Hq = a.num_heads;
   const int tok0 = part * P;
@@ -344,9 +216,9 @@ decode_partition_kernel(DecodeArgs a) {
 
   // The table slice of the whole partition range is fetched without waiting
   // for seq_len (it lies inside the table row either way), so the two loads
-  // overlap; entries past the sequence's end are never used.
+  // overlap.
   int bt_id = -1;
-  if (tid < P / B && blk0 + tid < a.max_blocks) bt_id = a.block_tables[(int64_t)s * a.max_blocks + blk0 + tid];
+  if (tid < nbp && blk0 + tid < a.max_blocks) bt_id = a.block_tables[(int64_t)s * a.max_blocks + blk0 + tid];
   int L = a.seq_lens[s];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const bool direct = L <= P;
@@ -357,273 +229,239 @@ decode_partition_kernel(DecodeArgs a) {
     return;
   }
   const int ntok = min(P, L - tok0) > 0 ? min(P, L - tok0) : 0;
-  const int nblk = (ntok + B - 1) / B;
 
   int* s_bt = reinterpret_cast<int*>(smem + lay.bt_off);
-  float* s_p = reinterpret_cast<float*>(smem + lay.p_off) + w * lay.p_wave;
-  // f16 path: probabilities of token pairs (t, t + TS) packed as f16x2, one
-  // dword per (pair, head), pair index jc*CH/2 + (i/2)*TS + ts for the token
-  // loaded by PV load i of chunk jc in slot ts.
-  uint32_t* s_h = reinterpret_cast<uint32_t*>(smem + lay.h_off) + w * lay.h_wave;
-  constexpr bool kDot2PV = std::is_same<QT, f16_t>::value;
-  // Wave w's partial output, once its PV pass is done: [G][D] floats at the
-  // start of region w.
-  float* s_o = reinterpret_cast<float*>(smem + lay.p_off);
+  float* s_o = reinterpret_cast<float*>(smem + lay.o_off);
   float* s_m = reinterpret_cast<float*>(smem + lay.m_off);
   float* s_l = reinterpret_cast<float*>(smem + lay.l_off);
 
   // 1. Block-table slice -> LDS.  Entries outside the pool become -1.
-  if (tid < P / B) s_bt[tid] = (bt_id < 0 || bt_id >= a.cache.num_blocks) ? -1 : bt_id;
+  if (tid < nbp) s_bt[tid] = (bt_id < 0 || bt_id >= a.cache.num_blocks) ? -1 : bt_id;
 
-  // The G query rows of this KV head are fetched once per workgroup into LDS
-  // (G*D elements, 16 bytes per thread); every lane then reads its slices
-  // from there, eight lanes per address.
-  QT* s_q = reinterpret_cast<QT*>(smem + lay.q_off);
+  // 2. Query operand: lane (head r, group grp) holds, for K load ls, the
+  // query elements 4*CE*ls + CE*grp .. + CE-1 of head r (zero for r >= G).
+  u32x4 qw[NLK][QW];
   {
-    const QT* qb = reinterpret_cast<const QT*>(a.query) + ((int64_t)s * Hq + g * G) * D;
-    for (int c = tid; c < G * D / QVEC; c += NT)
-      *reinterpret_cast<u32x4*>(s_q + c * QVEC) = *reinterpret_cast<const u32x4*>(qb + c * QVEC);
+    const QT* qrow = reinterpret_cast<const QT*>(a.query) + ((int64_t)s * Hq + g * G + (r < G ? r : 0)) * D;
+#pragma unroll
+    for (int ls = 0; ls < NLK; ++ls)
+#pragma unroll
+      for (int q = 0; q < QW; ++q)
+        qw[ls][q] = r < G ? *reinterpret_cast<const u32x4*>(qrow + 4 * CE * ls + CE * grp + q * (16 / (int)sizeof(QT)))
+                          : u32x4{0, 0, 0, 0};
   }
-  __syncthreads();
+  __syncthreads();  // table slice visible
 
-  // Query slices for the QK layout: lane `sub` of a token holds, for each
-  // head, dims c*LPT*VEC + sub*VEC .. +VEC of every chunk c.
-  const int sub = lane & (LPT - 1);
-  const int tq = lane / LPT;
-  u32x4 qv[G][NCK * KW];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < NCK; ++c)
-#pragma unroll
-      for (int w2 = 0; w2 < KW; ++w2)
-        qv[h][c * KW + w2] = *reinterpret_cast<const u32x4*>(s_q + h * D + c * LPT * VEC + sub * VEC + w2 * QVEC);
-
-  // This wave's blocks: local index jl -> partition block w + jl*NW.
-  const int nbw = nblk > w ? (nblk - w + kNW - 1) / kNW : 0;
   const int64_t blk_stride = (int64_t)Hkv * B * D;
   const T* kbase = reinterpret_cast<const T*>(a.cache.key_cache) + (int64_t)g * B * D;
-  const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * B * D;
+  const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * D * B;
   // FP8: widened K values are the codes' values * 2^-8.
   const float qscale = kFp8 ? a.scale * kLog2e * 256.f * a.cache.k_scale : a.scale * kLog2e;
-  const int myhead = sub >> SHIFT;
-  const bool writer = (sub & ((1 << SHIFT) - 1)) == 0;
 
-  // 2. QK with the next chunk's K in flight while the current one is used.
-  // Wave-local chunk jc is chunk jc % CPB of partition block w + (jc / CPB)*NW;
-  // its logits live at wave-local tokens jc*CH ...
-  const int nch = nbw * CPB;
-  float run_max = -INFINITY;
-  auto chunk_src = [&](const T* base, int jc, int& t0) -> const T* {
-    const int jb = w + (jc / CPB) * kNW;
-    t0 = jb * B + (jc % CPB) * CH;  // first token of the chunk, partition-relative
-    const int pb = s_bt[jb];
-    return pb >= 0 ? base + pb * blk_stride + (jc % CPB) * CH * D : nullptr;
+  struct Buf {
+    u32x4 k[2][NLK];        // K rows of the two 16-token halves
+    uint32_t v[NDT][VW];    // V^T: 8 tokens of dim 16*dd + r
   };
-  auto k_load = [&](u32x4 (&kb)[GPC][NCK], int jc) {
-    int t0;
-    const T* src = chunk_src(kbase, jc, t0);
-    if (src) {
+  auto load = [&](Buf& b, int st) {
+    const int stok = st * kStep;
 #pragma unroll
-      for (int gi = 0; gi < GPC; ++gi)
+    for (int c = 0; c < 2; ++c) {
+      const int t = stok + 8 * (r >> 2) + 4 * c + (r & 3);
+      const int j = t / B;
+      const int pb = (t < ntok && j < nbp) ? s_bt[j] : -1;
+      const T* src = kbase + (int64_t)pb * blk_stride + (t % B) * D + CE * grp;
 #pragma unroll
-        for (int c = 0; c < NCK; ++c)
-          kb[gi][c] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(src + (gi * TPG + tq) * D + c * LPT * VEC + sub * VEC));
+      for (int ls = 0; ls < NLK; ++ls)
+        b.k[c][ls] = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 4 * CE * ls))
+                             : u32x4{0, 0, 0, 0};
     }
-  };
-  auto qk_block = [&](const u32x4 (&kb)[GPC][NCK], int jc) {
-    int t0;
-    const bool valid = chunk_src(kbase, jc, t0) != nullptr;
+    const int t0 = stok + 8 * grp;
+    const int j = t0 / B;
+    const int pb = (t0 < ntok && j < nbp) ? s_bt[j] : -1;
+    const T* vsrc = vbase + (int64_t)pb * blk_stride + r * B + (t0 % B);
 #pragma unroll
-    for (int gi = 0; gi < GPC; ++gi) {
-      u32x4 ko[NCK * KW];
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) KOps<T>::widen(kb[gi][c], ko + c * KW);
-      float acc[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float x = 0.f;
-#pragma unroll
-        for (int c = 0; c < NCK * KW; ++c) x = dot16<QT>(qv[h][c], ko[c], x);
-        acc[h] = x;
-      }
-      float z = reduce_scatter8<G>(acc, sub);
-      const int tl = t0 + gi * TPG + tq;
-      z = (valid && tl < ntok) ? z * qscale : -INFINITY;
-      run_max = fmaxf(run_max, z);
-      if (writer) s_p[(jc * CH + gi * TPG + tq) * G + myhead] = z;
-    }
-  };
-  {
-    u32x4 kb0[GPC][NCK], kb1[GPC][NCK];
-    if (nch > 0) k_load(kb0, 0);
-    for (int jc = 0; jc < nch; jc += 2) {
-      if (jc + 1 < nch) k_load(kb1, jc + 1);
-      qk_block(kb0, jc);
-      if (jc + 2 < nch) k_load(kb0, jc + 2);
-      if (jc + 1 < nch) qk_block(kb1, jc + 1);
-    }
-  }
-
-  // The first V chunk goes out before the softmax so HBM stays busy.
-  auto v_load = [&](VLoad (&vb)[IPC], int jc) {
-    int t0;
-    const T* src = chunk_src(vbase, jc, t0);
-    if (src) {
-      const int ts = lane / LPV, dc = lane % LPV;
-#pragma unroll
-      for (int i = 0; i < IPC; ++i)
-        vb[i] = __builtin_nontemporal_load(reinterpret_cast<const VLoad*>(src + (i * TS + ts) * D + dc * VV));
-    }
-  };
-  VLoad vb0[IPC], vb1[IPC];
-  if (nch > 0) v_load(vb0, 0);
-
-  // 3. Wave-local softmax.  Lanes with equal `sub` hold the same head.
-  run_max = fmaxf(run_max, shfl_xor(run_max, 8));
-  run_max = fmaxf(run_max, shfl_xor(run_max, 16));
-  run_max = fmaxf(run_max, shfl_xor(run_max, 32));
-  // Lane `lane` now serves head lane % G (64 % G == 0): fetch that head's max.
-  const float M = __shfl(run_max, (lane % G) << SHIFT, 64);
-  wave_lds_sync();
-  float lsum = 0.f;
-  {
-    const int ne = nch * CH * G;
-    for (int e = lane; e < ne; e += 64) {
-      const float z = s_p[e];
-      float pr = z == -INFINITY ? 0.f : fast_exp2(z - M);
-      if constexpr (kDot2PV) {
-        // The PV product sees p rounded to f16; the normaliser sums the
-        // same rounded values.
-        const _Float16 ph = (_Float16)pr;
-        pr = (float)ph;
-        const int tw = e / G, hh = e % G;        // wave-local token, head
-        const int jc = tw / CH, tb = tw % CH;    // chunk, token within chunk
-        const int i = tb / TS, tsl = tb % TS;    // PV load index, slot
-        const int pair = jc * (CH / 2) + (i / 2) * TS + tsl;
-        reinterpret_cast<uint16_t*>(s_h)[(pair * G + hh) * 2 + (i & 1)] = __builtin_bit_cast(uint16_t, ph);
+    for (int dd = 0; dd < NDT; ++dd) {
+      const T* p = vsrc + dd * 16 * B;
+      if constexpr (VW == 2) {
+        const u32x2 x = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)) : u32x2{0, 0};
+        b.v[dd][0] = x[0], b.v[dd][1] = x[1];
       } else {
-        s_p[e] = pr;
+#pragma unroll
+        for (int h = 0; h < VW / 4; ++h) {
+          const u32x4 x = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + h) : u32x4{0, 0, 0, 0};
+          b.v[dd][4 * h] = x[0], b.v[dd][4 * h + 1] = x[1], b.v[dd][4 * h + 2] = x[2], b.v[dd][4 * h + 3] = x[3];
+        }
       }
-      lsum += pr;
     }
-  }
-#pragma unroll
-  for (int m = G; m < 64; m <<= 1) lsum += shfl_xor(lsum, m);
-  wave_lds_sync();
+  };
 
-  // 4. PV, double-buffered like QK.
-  float o[NV];
+  f32x4 o[NDT];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) o[k] = 0.f;
-  const int ts = lane / LPV;
-  auto pv_block = [&](const VLoad (&vb)[IPC], int jc) {
-    int t0;
-    if (!chunk_src(vbase, jc, t0)) return;
-    if constexpr (kDot2PV) {
-      // Token pairs (load i, load i+1) of this slot: build (v_t0[d], v_t1[d])
-      // halves with v_perm and dot them with the packed (p_t0, p_t1).
+  for (int dd = 0; dd < NDT; ++dd) o[dd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](Buf& b, int st) {
+    // S = K . Q^T for the two halves: lane (head r, group grp) receives the
+    // logits of tokens 8*grp + 4*c + jj.
+    f32x4 sc[2];
 #pragma unroll
-      for (int i = 0; i < IPC; i += 2) {
-        VLoad va = vb[i], vz = vb[i + 1];
-        // Tail of the last block: zero V of tokens past the end (p is 0
-        // there, and 0 * NaN would poison the sum).
-        if (t0 + i * TS + ts >= ntok) va = VLoad(0u);
-        if (t0 + (i + 1) * TS + ts >= ntok) vz = VLoad(0u);
-        uint32_t X[VV];
-        if constexpr (kFp8) {
-          // Byte j of each token's word -> bits 15:8 / 31:24, then widen.
+    for (int c = 0; c < 2; ++c) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const uint32_t lo = va[q], hi = vz[q];
+      for (int ls = 0; ls < NLK; ++ls) {
+        if constexpr (kF32) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              X[4 * q + j] = e4m3_pair_to_f16x2(
-                  __builtin_amdgcn_perm(hi, lo, ((4u + j) << 24) | (0x0cu << 16) | ((uint32_t)j << 8) | 0x0cu));
+          for (int sub = 0; sub < 4; ++sub) {
+            const uint32_t kv = b.k[c][ls][sub], qv = qw[ls][0][sub];
+            acc = mma_f32(__uint_as_float(kv), __uint_as_float(qv), acc);
           }
+        } else if constexpr (kFp8) {
+#pragma unroll
+          for (int sub = 0; sub < NSUB; ++sub) {
+            u32x4 ka;
+            uint32_t x0, x1, x2, x3;
+            widen4(b.k[c][ls][2 * sub], x0, x1);
+            widen4(b.k[c][ls][2 * sub + 1], x2, x3);
+            ka = u32x4{x0, x1, x2, x3};
+            acc = mma_f16(ka, qw[ls][sub], acc);
+          }
+        } else if constexpr (kBf16) {
+          acc = mma_bf16(b.k[c][ls], qw[ls][0], acc);
         } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = va[q], hi = vz[q];
-            X[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-            X[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-          }
+          acc = mma_f16(b.k[c][ls], qw[ls][0], acc);
         }
-        const int pair = jc * (CH / 2) + (i / 2) * TS + ts;
-        uint32_t pw[G];
-        const uint32_t* pp = s_h + pair * G;
-        if constexpr (G % 4 == 0) {
+      }
+      sc[c] = acc;
+    }
+
+    // Online softmax.  Tokens of this lane: 8*grp + e, e = 4*c + jj.
+    const int t0 = st * kStep + 8 * grp;
+    const int jb = t0 / B;
+    const bool blk_ok = t0 < ntok && jb < nbp && s_bt[jb] >= 0;
+    const int nvalid = blk_ok ? min(8, ntok - t0) : 0;
+    float z[8];
 #pragma unroll
-          for (int h = 0; h < G; h += 4) {
-            const u32x4 v4 = *reinterpret_cast<const u32x4*>(pp + h);
-            pw[h] = v4[0], pw[h + 1] = v4[1], pw[h + 2] = v4[2], pw[h + 3] = v4[3];
-          }
+    for (int e = 0; e < 8; ++e) z[e] = e < nvalid ? sc[e / 4][e % 4] * qscale : -INFINITY;
+    float mx = z[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = z[e] == -INFINITY ? 0.f : fast_exp2(z[e] - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int dd = 0; dd < NDT; ++dd) o[dd] *= alpha;
+
+    // Value tokens past the end (or in a block outside the pool) are zeroed:
+    // their probabilities are 0 and 0 * NaN would poison the sums.
+    if (nvalid < 8) {
+#pragma unroll
+      for (int q = 0; q < VW; ++q) {
+        uint32_t keep;
+        if constexpr (VW == 8) {
+          keep = q < nvalid ? 0xffffffffu : 0u;
+        } else if constexpr (VW == 4) {
+          keep = 2 * q >= nvalid ? 0u : (2 * q + 1 >= nvalid ? 0xffffu : 0xffffffffu);
         } else {
+          keep = 0;
 #pragma unroll
-          for (int h = 0; h < G; ++h) pw[h] = pp[h];
+          for (int bb = 0; bb < 4; ++bb) keep |= (4 * q + bb < nvalid ? 0xffu : 0u) << (8 * bb);
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const f16x2 ph = __builtin_bit_cast(f16x2, pw[h]);
+        for (int dd = 0; dd < NDT; ++dd) b.v[dd][q] &= keep;
+      }
+    }
+
+    // O^T += V^T . P^T
+    float lstep = 0.f;
+    if constexpr (kF32) {
 #pragma unroll
-          for (int v = 0; v < VV; ++v)
-            o[h * VV + v] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(f16x2, X[v]), o[h * VV + v], false);
-        }
+      for (int e = 0; e < 8; ++e) lstep += p[e];
+#pragma unroll
+      for (int dd = 0; dd < NDT; ++dd)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[dd] = mma_f32(__uint_as_float(b.v[dd][e]), p[e], o[dd]);
+    } else if constexpr (kBf16) {
+      // p = hi + lo, both bf16: the product keeps ~16 bits of p.
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = p[2 * q], a1 = p[2 * q + 1];
+        const uint32_t h = pack_bf16(a0, a1);
+        ph[q] = h;
+        pl[q] = pack_bf16(a0 - bf16_lo(h), a1 - bf16_hi(h));
+        lstep += a0 + a1;
+      }
+      const u32x4 pa = {ph[0], ph[1], ph[2], ph[3]}, pb = {pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+      for (int dd = 0; dd < NDT; ++dd) {
+        const u32x4 va = {b.v[dd][0], b.v[dd][1], b.v[dd][2], b.v[dd][3]};
+        o[dd] = mma_bf16(va, pa, o[dd]);
+        o[dd] = mma_bf16(va, pb, o[dd]);
       }
     } else {
+      // f16 (and widened FP8): p rounded to f16; the normaliser sums the
+      // same rounded values.
+      uint32_t ph[4];
 #pragma unroll
-    for (int i = 0; i < IPC; ++i) {
-      const int tb = i * TS + ts;  // token within the chunk
-      if (t0 + tb >= ntok) continue;  // tail of the last block: never touch its contents
-      float pr[G];
-      const float* pp = s_p + (jc * CH + tb) * G;
-      if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int h = 0; h < G; h += 4) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4*>(pp + h);
-          pr[h] = v4[0], pr[h + 1] = v4[1], pr[h + 2] = v4[2], pr[h + 3] = v4[3];
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) pr[h] = pp[h];
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h = pack_f16(p[2 * q], p[2 * q + 1]);
+        ph[q] = h;
+        lstep += f16_lo(h) + f16_hi(h);
       }
-      float vf[VV];
-      unpack16<T>(vb[i], vf);
+      const u32x4 pa = {ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int v = 0; v < VV; ++v) o[h * VV + v] = fmaf(pr[h], vf[v], o[h * VV + v]);
+      for (int dd = 0; dd < NDT; ++dd) {
+        u32x4 va;
+        if constexpr (kFp8) {
+          uint32_t x0, x1, x2, x3;
+          widen4(b.v[dd][0], x0, x1);
+          widen4(b.v[dd][1], x2, x3);
+          va = u32x4{x0, x1, x2, x3};
+        } else {
+          va = u32x4{b.v[dd][0], b.v[dd][1], b.v[dd][2], b.v[dd][3]};
+        }
+        o[dd] = mma_f16(va, pa, o[dd]);
+      }
     }
-    }
+    l_run = l_run * alpha + lstep;
   };
-  for (int jc = 0; jc < nch; jc += 2) {
-    if (jc + 1 < nch) v_load(vb1, jc + 1);
-    pv_block(vb0, jc);
-    if (jc + 2 < nch) v_load(vb0, jc + 2);
-    if (jc + 1 < nch) pv_block(vb1, jc + 1);
+
+  // 3. The wave's steps w, w + kNW, ..., NBUF of them in flight.
+  const int nsteps = (ntok + kStep - 1) / kStep;
+  const int nmine = nsteps > w ? (nsteps - w + kNW - 1) / kNW : 0;
+  Buf buf[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i)
+    if (i < nmine) load(buf[i], w + i * kNW);
+  for (int i0 = 0; i0 < nmine; i0 += NBUF) {
+#pragma unroll
+    for (int bi = 0; bi < NBUF; ++bi) {
+      const int i = i0 + bi;
+      if (i < nmine) {
+        compute(buf[bi], w + i * kNW);
+        if (i + NBUF < nmine) load(buf[bi], w + (i + NBUF) * kNW);
+      }
+    }
   }
 
-  // 5. Fold token slots, park the wave's partial in LDS, merge the waves.
-  reduce_slots<NV, TS>(o);
-  wave_lds_sync();  // this wave's probability reads are done before its region is reused
-  {
-    constexpr int R = TS < 4 ? TS : 4;
-    constexpr int PER = NV / R;  // values per lane after the fold
-    const int q = lane / (64 / R);
-    const int col = lane % (64 / R);
-    if (col < LPV) {
+  // 4. The wave's partials -> LDS, then merge the waves.  Lane (head r,
+  // group grp) holds dims 16*dd + 4*grp + jj; the four groups' sums add up.
+  float l_tot = l_run + shfl_xor(l_run, 16);
+  l_tot += shfl_xor(l_tot, 32);
+  if (r < G) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int k = q * PER + j;
-        const int h = k / VV, v = k % VV;
-        s_o[w * lay.p_wave + h * D + col * VV + v] = o[j];
-      }
+    for (int dd = 0; dd < NDT; ++dd)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) s_o[(w * G + r) * D + 16 * dd + 4 * grp + jj] = o[dd][jj];
+    if (grp == 0) {
+      s_m[w * G + r] = m_run;
+      s_l[w * G + r] = l_tot;
     }
-  }
-  if (lane < G) {
-    s_m[w * G + lane] = M;
-    s_l[w * G + lane] = lsum;
   }
   __syncthreads();
 
@@ -640,13 +478,13 @@ decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int ww = 0; ww < kNW; ++ww) {
         const float mw = s_m[ww * G + h];
-        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - Mx);
-        acc = fmaf(sc, s_o[ww * lay.p_wave + h * D + d], acc);
-        l = fmaf(sc, s_l[ww * G + h], l);
+        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - Mx);
+        acc = fmaf(f, s_o[(ww * G + h) * D + d], acc);
+        l = fmaf(f, s_l[ww * G + h], l);
       }
     }
-    const int hq = g * G + h;
     acc *= vfac;
+    const int hq = g * G + h;
     if (direct) {
       QT* out = reinterpret_cast<QT*>(a.out) + ((int64_t)s * Hq + hq) * D + d;
       store_elem<QT>(out, l > 0.f ? acc / l : 0.f);
@@ -684,7 +522,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_seq_len > a.partition) {
-    hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
+    hipLaunchKernelGGL((decode_reduce_kernel<typename Dec<T>::Q, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
                        stream, a);
     e = hipGetLastError();
   }
@@ -713,16 +551,11 @@ hipError_t dispatch_b(const DecodeArgs& a, int G, hipStream_t stream) {
 
 template <typename T>
 hipError_t dispatch_d(const DecodeArgs& a, int G, hipStream_t stream) {
-  if constexpr (Elem<T>::kBytes == 1) {
-    // 16 codes per lane per token need 8 x 16 = 128 dims.
-    return a.cache.head_dim == 128 ? dispatch_b<T, 128>(a, G, stream) : hipErrorInvalidValue;
-  } else {
-    switch (a.cache.head_dim) {
-      case 64: return dispatch_b<T, 64>(a, G, stream);
-      case 128: return dispatch_b<T, 128>(a, G, stream);
-    }
-    return hipErrorInvalidValue;
+  switch (a.cache.head_dim) {
+    case 64: return dispatch_b<T, 64>(a, G, stream);
+    case 128: return dispatch_b<T, 128>(a, G, stream);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -13,7 +13,7 @@
 // Work decomposition.  A workgroup (4 waves) owns 128 query rows that share
 // one KV head: the G heads of the group times 128/G consecutive positions.
 // Each wave owns 32 rows.  Keys stream through in tiles of 32: the tile's K
-// rows ([32][D]) and V rows, transposed to [D][32], are staged in LDS
+// rows ([32][D]) and V^T ([D][32], as the pool stores value tiles) are staged in LDS
 // (double-buffered: the next tile's global loads are in flight while the
 // current tile is used), then per wave
 //   S^T[32 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16 over D
@@ -187,10 +187,11 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   };
 
   // Global -> registers for one tile.  K chunks: key-major (coalesced rows);
-  // V chunks: key-fastest, so the transposed LDS writes of a wave hit
-  // consecutive banks.  Keys no row of this workgroup sees (>= kend), or in
-  // blocks outside the pool, read as zeros (their probabilities are zero; a
-  // zero V keeps 0 * V finite).
+  // V chunks: 8 keys of one dimension from the transposed value tile (a
+  // tile of 32 keys never splits an 8-key piece across blocks, since 8
+  // divides the block size), copied to LDS as they are.  Keys no row of this
+  // workgroup sees (>= kend), or in blocks outside the pool, read as zeros
+  // (their probabilities are zero; a zero V keeps 0 * V finite).
   u32x4 kreg[CPT], vreg[CPT];
   auto fetch = [&](int t) {
 #pragma unroll
@@ -207,12 +208,22 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
         kreg[i] = x;
       }
       {
-        const int key = c % kKT, dch = c / kKT;
-        const int pos = t * kKT + key;
+        const int kg = c % (kKT / 8), d = c / (kKT / 8);
+        const int pos = t * kKT + kg * 8;
         u32x4 x = {0, 0, 0, 0};
         if (pos < kend) {  // keys >= kend are masked for every row of this tile
           const int pb = block_of(pos);
-          if (pb >= 0) x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+          if (pb >= 0) {
+            x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * D + d) * B + pos % B);
+            const int nv = kend - pos;  // keys of this piece that some row sees
+            if (nv < 8) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t keep = 2 * e >= nv ? 0u : (2 * e + 1 >= nv ? 0xffffu : 0xffffffffu);
+                x[e] &= keep;
+              }
+            }
+          }
         }
         vreg[i] = x;
       }
@@ -227,14 +238,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
         *reinterpret_cast<u32x4*>(Ks(buf) + key * S::kKStride + dch * 8) = kreg[i];
       }
       {
-        const int key = c % kKT, dch = c / kKT;
-        uint16_t* col = Vt(buf) + (dch * 8) * S::kVStride + key;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wv = vreg[i][e];
-          col[(2 * e) * S::kVStride] = (uint16_t)(wv & 0xffffu);
-          col[(2 * e + 1) * S::kVStride] = (uint16_t)(wv >> 16);
-        }
+        const int kg = c % (kKT / 8), d = c / (kKT / 8);
+        *reinterpret_cast<u32x4*>(Vt(buf) + d * S::kVStride + kg * 8) = vreg[i];
       }
     }
   };

@@ -180,6 +180,12 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def value_shape(key_shape):
+    """Shape of the value pool that goes with a key pool of ``key_shape``."""
+    NB, H, B, D = key_shape
+    return (NB, H, D, B)
+
+
 def is_fp8(key_cache: torch.Tensor) -> bool:
     return _DTYPE.get(key_cache.dtype) == PA_FP8_E4M3
 
@@ -190,14 +196,17 @@ def io_dtype(key_cache: torch.Tensor) -> torch.dtype:
 
 
 def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor, scales=None) -> pa_kv_cache:
-    """Describe a pool of shape [num_blocks, num_kv_heads, block_size, head_dim].
+    """Describe a pool: keys [num_blocks, num_kv_heads, block_size, head_dim],
+    values [num_blocks, num_kv_heads, head_dim, block_size] (each value tile
+    transposed).
 
     ``scales`` = (k_scale, v_scale) is required for an FP8 pool: a code c
     stands for value(c) * scale."""
     _need(key_cache, "key_cache")
     _need(value_cache, "value_cache", key_cache.dtype)
-    if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
-        raise ValueError("key_cache/value_cache must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if key_cache.dim() != 4 or value_cache.dim() != 4 or value_cache.shape != value_shape(key_cache.shape):
+        raise ValueError("key_cache must be [num_blocks, num_kv_heads, block_size, head_dim] and value_cache "
+                         "[num_blocks, num_kv_heads, head_dim, block_size]")
     if key_cache.dtype not in _DTYPE:
         raise ValueError(f"unsupported cache dtype {key_cache.dtype}")
     if is_fp8(key_cache) and scales is None:
@@ -327,9 +336,9 @@ def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
     _check(lib().pa_copy_blocks(ctypes.byref(c), src.data_ptr(), dst.data_ptr(), src.numel(), _stream(stream)), "pa_copy_blocks")
 
 
-def _buf_ok(t, key_cache, n, name):
-    if t.dtype != key_cache.dtype or not t.is_contiguous() or tuple(t.shape) != (n, *key_cache.shape[1:]):
-        raise ValueError(f"{name} must be contiguous [{n}, *block shape] in the cache dtype")
+def _buf_ok(t, pool, n, name):
+    if t.dtype != pool.dtype or not t.is_contiguous() or tuple(t.shape) != (n, *pool.shape[1:]):
+        raise ValueError(f"{name} must be contiguous [{n}, *block shape of its pool] in the cache dtype")
     if not (t.is_cuda or t.is_pinned()):
         raise ValueError(f"{name} must be device memory or pinned host memory")
 
@@ -339,7 +348,7 @@ def pa_gather_blocks(key_cache, value_cache, block_ids, key_out, value_out, stre
     _need(block_ids, "block_ids", torch.int32)
     n = block_ids.numel()
     _buf_ok(key_out, key_cache, n, "key_out")
-    _buf_ok(value_out, key_cache, n, "value_out")
+    _buf_ok(value_out, value_cache, n, "value_out")
     _check(lib().pa_gather_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_out.data_ptr(), value_out.data_ptr(),
                                   _stream(stream)), "pa_gather_blocks")
 
@@ -349,7 +358,7 @@ def pa_scatter_blocks(key_cache, value_cache, block_ids, key_in, value_in, strea
     _need(block_ids, "block_ids", torch.int32)
     n = block_ids.numel()
     _buf_ok(key_in, key_cache, n, "key_in")
-    _buf_ok(value_in, key_cache, n, "value_in")
+    _buf_ok(value_in, value_cache, n, "value_in")
     _check(lib().pa_scatter_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_in.data_ptr(), value_in.data_ptr(),
                                    _stream(stream)), "pa_scatter_blocks")
 

@@ -12,7 +12,9 @@ Sources (web pages on paged KV caches):
 
 Layout (one layer's pool, [P1] "KV Cache 的内存开销与分页机制": fixed-size
 physical blocks, a per-request block table):
-  key_cache, value_cache : [num_blocks, num_kv_heads, block_size, head_dim]
+  key_cache              : [num_blocks, num_kv_heads, block_size, head_dim]
+  value_cache            : [num_blocks, num_kv_heads, head_dim, block_size]
+                           (each value tile transposed)
   block_tables           : int32 [num_seqs, max_blocks_per_seq]
   seq_lens               : int32 [num_seqs], tokens in the cache after this
                            step's new tokens are written (they are counted)
@@ -237,7 +239,9 @@ def build(
     Hkv, D, Hq = num_kv_heads, head_dim, num_heads
     shape = (NB, Hkv, B, D)
     kc = f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
-    vc = f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
+    # Values are drawn in the same (block, head, token, dim) order as keys
+    # and stored with each tile transposed: [NB, Hkv, D, B].
+    vc = np.ascontiguousarray(f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype).transpose(0, 1, 3, 2))
     T = int(q_lens.sum())
     nk = f32_to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32), dtype)
     nv = f32_to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32), dtype)
@@ -256,7 +260,7 @@ def build(
         dead = ~live
         nanv = nan_value(dtype)
         kc.transpose(0, 2, 1, 3)[dead] = nanv
-        vc.transpose(0, 2, 1, 3)[dead] = nanv
+        vc.transpose(0, 3, 1, 2)[dead] = nanv
 
     return Workload(
         name=name,

@@ -188,9 +188,9 @@ def fp8_pool_gpu(gw: GpuWorkload, scales):
 
     NB, H, B, D = gw.key_cache.shape
     kc8 = torch.zeros((NB, H, B, D), dtype=torch.uint8, device=gw.key_cache.device)
-    vc8 = torch.zeros_like(kc8)
+    vc8 = torch.zeros((NB, H, D, B), dtype=torch.uint8, device=gw.key_cache.device)
     rows_k = gw.key_cache.permute(0, 2, 1, 3).reshape(NB * B, H, D).contiguous()
-    rows_v = gw.value_cache.permute(0, 2, 1, 3).reshape(NB * B, H, D).contiguous()
+    rows_v = gw.value_cache.permute(0, 3, 1, 2).reshape(NB * B, H, D).contiguous()
     slots = torch.arange(NB * B, dtype=torch.int64, device=gw.key_cache.device)
     pa.pa_reshape_and_cache(kc8, vc8, rows_k, rows_v, slots, scales=scales)
     return kc8, vc8

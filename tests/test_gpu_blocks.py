@@ -56,9 +56,9 @@ def test_gather_scatter_round_trip(pinned):
     gw = harness.GpuWorkload(w)
     ids = np.random.default_rng(3).choice(w.num_blocks, 12, replace=False).astype(np.int32)
     idt = torch.from_numpy(ids).cuda()
-    shape = (len(ids), *gw.key_cache.shape[1:])
     kw = dict(dtype=gw.key_cache.dtype, pin_memory=True) if pinned else dict(dtype=gw.key_cache.dtype, device="cuda")
-    kb, vb = torch.empty(shape, **kw), torch.empty(shape, **kw)
+    kb = torch.empty((len(ids), *gw.key_cache.shape[1:]), **kw)
+    vb = torch.empty((len(ids), *gw.value_cache.shape[1:]), **kw)
     pa.pa_gather_blocks(gw.key_cache, gw.value_cache, idt, kb, vb)  # swap out
     torch.cuda.synchronize()
     assert np.array_equal(harness.from_device(kb, w.dtype).view(np.uint8), oracle.gather_blocks(w.key_cache, ids).view(np.uint8))
@@ -94,7 +94,7 @@ def test_copy_on_write_fork_decodes_like_the_oracle():
     assert t0[:2] == t1[:2] and t0[2] == old and t1[2] == fresh
 
     kc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D), dtype=np.float32), dt)
-    vc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D), dtype=np.float32), dt)
+    vc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, D, B), dtype=np.float32), dt)  # value tiles [D][B]
     nk = synth.f32_to_storage(rng.standard_normal((2, Hkv, D), dtype=np.float32), dt)
     nv = synth.f32_to_storage(rng.standard_normal((2, Hkv, D), dtype=np.float32), dt)
     q = synth.f32_to_storage(rng.standard_normal((2, Hq, D), dtype=np.float32), dt)
@@ -116,7 +116,7 @@ def test_copy_on_write_fork_decodes_like_the_oracle():
     oracle.copy_blocks(v64, [old], [fresh])
     for s, blk in enumerate((old, fresh)):
         k64[blk, :, 37 % B] = oracle.to_float64(nk[s], dt)
-        v64[blk, :, 37 % B] = oracle.to_float64(nv[s], dt)
+        v64[blk, :, :, 37 % B] = oracle.to_float64(nv[s], dt)
     ref = oracle.decode_attention(oracle.to_float64(q, dt), k64, v64, tables, lens, 1 / np.sqrt(D))
     ok, maxerr, nbad = harness.tolerance_ok(oracle.to_float64(harness.from_device(out, dt), dt), ref, dt)
     assert ok, (maxerr, nbad)
@@ -150,7 +150,7 @@ def test_prefix_cache_hit_serves_chunked_prefill():
     ids_b = prompt + list(rng.integers(0, vocab, 20))
     bm = pa.BlockManager(NB, B, rng.permutation(NB))
     gk = torch.zeros((NB, Hkv, B, D), dtype=torch.float16, device="cuda")
-    gv = torch.zeros_like(gk)
+    gv = torch.zeros((NB, Hkv, D, B), dtype=torch.float16, device="cuda")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
 
     def write(sid, ids, start):
@@ -179,7 +179,7 @@ def test_prefix_cache_hit_serves_chunked_prefill():
     # Oracle: B's whole sequence recomputed into a pool of its own (identity table).
     k, v = kv(np.asarray(ids_b), 0)
     kc = np.zeros((6, Hkv, B, D))
-    vc = np.zeros((6, Hkv, B, D))
+    vc = np.zeros((6, Hkv, D, B))
     oracle.reshape_and_cache(kc, vc, oracle.to_float64(k, dt), oracle.to_float64(v, dt), np.arange(len(ids_b)))
     ref = oracle.prefill_attention(oracle.to_float64(q, dt), np.array([0, 20]), kc, vc, np.arange(6)[None, :],
                                    np.array([len(ids_b)]), 1 / np.sqrt(D))

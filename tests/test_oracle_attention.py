@@ -16,7 +16,7 @@ def _identity_pool(Kd, Vd, B):
     S, L, Hkv, D = Kd.shape
     nb = L // B
     kc = Kd.reshape(S, nb, B, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(S * nb, Hkv, B, D)
-    vc = Vd.reshape(S, nb, B, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(S * nb, Hkv, B, D)
+    vc = Vd.reshape(S, nb, B, Hkv, D).transpose(0, 1, 3, 4, 2).reshape(S * nb, Hkv, D, B)  # value tiles [D][B]
     tables = np.arange(S * nb, dtype=np.int32).reshape(S, nb)
     return np.ascontiguousarray(kc), np.ascontiguousarray(vc), tables
 
@@ -90,20 +90,20 @@ def test_decode_closed_forms():
     rng = np.random.default_rng(3)
     NB, Hkv, B, D, Hq = 6, 2, 4, 8, 4
     kc = rng.standard_normal((NB, Hkv, B, D))
-    vc = rng.standard_normal((NB, Hkv, B, D))
+    vc = rng.standard_normal((NB, Hkv, D, B))  # value tiles [D][B]
     tables = np.array([[3, 1, 5], [0, 2, 4]], np.int32)
     q = rng.standard_normal((2, Hq, D))
     # Length 1: the output is the first value vector, whatever the query.
     out = oracle.decode_attention(q, kc, vc, tables, np.array([1, 1]), 0.7)
     for s in range(2):
         for h in range(Hq):
-            np.testing.assert_allclose(out[s, h], vc[tables[s, 0], h // 2, 0], rtol=0, atol=1e-15)
+            np.testing.assert_allclose(out[s, h], vc[tables[s, 0], h // 2, :, 0], rtol=0, atol=1e-15)
     # Zero query: uniform weights, so the output is the mean of the values.
     out = oracle.decode_attention(np.zeros_like(q), kc, vc, tables, np.array([11, 7]), 1.0)
-    mean0 = np.concatenate([vc[b] for b in tables[0]], axis=1)[:, :11].mean(axis=1)  # [Hkv, D]
+    mean0 = np.concatenate([vc[b] for b in tables[0]], axis=2)[:, :, :11].mean(axis=2)  # [Hkv, D]
     np.testing.assert_allclose(out[0], np.repeat(mean0, 2, axis=0), atol=1e-14)
     # Constant value rows: output is that row.
-    vconst = np.broadcast_to(np.arange(D, dtype=np.float64), vc.shape).copy()
+    vconst = np.broadcast_to(np.arange(D, dtype=np.float64)[:, None], vc.shape).copy()
     out = oracle.decode_attention(q, kc, vconst, tables, np.array([9, 12]), 0.3)
     np.testing.assert_allclose(out, np.broadcast_to(np.arange(D), out.shape), atol=1e-13)
     # Length 0: zeros.
@@ -113,14 +113,14 @@ def test_decode_closed_forms():
     kd = np.zeros_like(kc)
     kd[tables[0, 1], :, 2, :] = 1.0
     out = oracle.decode_attention(np.ones_like(q) * 100, kd, vc, tables, np.array([10, 10]), 1.0)
-    np.testing.assert_allclose(out[0, 0], vc[tables[0, 1], 0, 2], atol=1e-12)
+    np.testing.assert_allclose(out[0, 0], vc[tables[0, 1], 0, :, 2], atol=1e-12)
 
 
 def test_decode_gqa_groups_are_contiguous_heads():
     # Hkv=2, Hq=4: heads 0,1 read KV head 0, heads 2,3 read KV head 1.
     rng = np.random.default_rng(4)
     kc = rng.standard_normal((2, 2, 4, 8))
-    vc = np.zeros((2, 2, 4, 8))
+    vc = np.zeros((2, 2, 8, 4))
     vc[:, 0] = 1.0
     vc[:, 1] = -1.0
     out = oracle.decode_attention(rng.standard_normal((1, 4, 8)), kc, vc, np.array([[1, 0]], np.int32), np.array([6]), 1.0)

@@ -115,11 +115,11 @@ def test_fp8_scatter_writes_quantised_codes():
     rng = np.random.default_rng(3)
     NB, H, B, D = 4, 2, 16, 8
     kc = np.full((NB, H, B, D), 0x55, np.uint8)
-    vc = kc.copy()
+    vc = np.full((NB, H, D, B), 0x55, np.uint8)
     key = rng.standard_normal((3, H, D)).astype(np.float16)
     val = rng.standard_normal((3, H, D)).astype(np.float16)
     slots = np.array([5, -1, 40])
     fp8.reshape_and_cache_fp8(kc, vc, key, val, slots, 0.05, 0.02)
     assert np.array_equal(kc[0, :, 5], fp8.fp8_quantize(key[0], 0.05))
-    assert np.array_equal(vc[2, :, 8], fp8.fp8_quantize(val[2], 0.02))
+    assert np.array_equal(vc[2, :, :, 8], fp8.fp8_quantize(val[2], 0.02))
     assert np.count_nonzero(kc != 0x55) <= 2 * H * D  # the padding token wrote nothing

@@ -120,12 +120,12 @@ def test_reshape_and_cache_round_trip_and_sentinel():
     # Exactly T slots changed in each pool; the rest keep the sentinel.
     changed = (kc != -7.0).all(axis=(1, 3))  # [NB, B]
     assert changed.sum() == T
-    assert ((vc != -9.0).all(axis=(1, 3))).sum() == T
+    assert ((vc != -9.0).all(axis=(1, 2))).sum() == T  # value tiles [D][B]: the slot is the last axis
 
 
 def test_reshape_and_cache_skips_negative_and_rejects_duplicates():
     kc = np.zeros((4, 2, 4, 3))
-    vc = np.zeros((4, 2, 4, 3))
+    vc = np.zeros((4, 2, 3, 4))
     K = np.ones((3, 2, 3))
     V = 2 * np.ones((3, 2, 3))
     oracle.reshape_and_cache(kc, vc, K, V, np.array([5, -1, 15]))
