@@ -152,7 +152,11 @@ pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* va
                        int32_t max_q_len, int64_t* slot_mapping, int32_t num_tokens,
                        hipStream_t stream);
 
-/* Partition length (tokens) that pa_decode picks when partition_size is 0. */
+/* Partition length (tokens) that pa_decode picks when partition_size is 0:
+ * with at most 256 (sequence, KV head) pairs, each sequence is cut into the
+ * equal parts that give about one workgroup per compute unit (one part when
+ * the pairs alone fill the chip); with more pairs, 1024 tokens, halved while
+ * that leaves fewer than two workgroups per compute unit.  At most 4096. */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                                  int32_t block_size);
 
@@ -191,12 +195,37 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query,
                     size_t workspace_bytes, hipStream_t stream);
 
 /* pa_decode with an explicit partition length in tokens: a positive multiple
- * of block_size no larger than 1024 (0 = automatic). */
+ * of block_size no larger than 4096 (0 = automatic). */
 pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                        int32_t max_seq_len, float scale, void* workspace,
                        size_t workspace_bytes, int32_t partition_size, hipStream_t stream);
+
+/* The two launches of pa_decode_ex, for callers that time or interleave
+ * them.  stage 1: the partition kernel (writes the output of every sequence
+ * that fits one partition and the partials of the others to the workspace);
+ * stage 2: the merge of those partials (launches nothing when max_seq_len
+ * fits one partition).  Arguments as for pa_decode_ex, identical for both
+ * stages; stage 2 must follow stage 1 on the same stream.  Any other stage
+ * value returns PA_ERR_SHAPE. */
+pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t max_seq_len, float scale, void* workspace,
+                          size_t workspace_bytes, int32_t partition_size, int32_t stage,
+                          hipStream_t stream);
+
+/* pa_decode_ex with the partition kernel's own start and end recorded into
+ * two caller-created HIP events (hipExtLaunchKernel): the duration of the
+ * dominant launch, measured without a marker packet between the partition
+ * and merge launches.  Either event may be NULL. */
+pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t max_seq_len, float scale, void* workspace,
+                          size_t workspace_bytes, int32_t partition_size, hipEvent_t kernel_start,
+                          hipEvent_t kernel_stop, hipStream_t stream);
 
 /* Chunked-prefill attention over the paged cache (causal).  [P1]
  * "工程边界与架构取舍": prefill is a compute-bound matrix product and a long

@@ -170,15 +170,27 @@ pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, 
 }
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size) {
-  // Aim for at least two (4-wave) workgroups per compute unit; longer
-  // partitions amortise each workgroup's start-up and the merge, shorter
-  // ones fill the chip when there are few (sequence, KV head) pairs.
+  // Few (sequence, KV head) pairs: split every sequence into as many equal
+  // partitions as make about one 8-wave workgroup per compute unit, so that
+  // one round of workgroups covers the batch with the fewest partials to
+  // merge (a single partition when the pairs alone fill the chip).  Many
+  // pairs: 1024-token partitions on 4-wave workgroups, halved while that
+  // gives fewer than two workgroups per compute unit.
   if (block_size <= 0) return 0;
   const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-  int p = pa::kMaxPartition;
-  while (p > 128 && pairs * ceil_div(max_seq_len > 0 ? max_seq_len : 1, p) < 2 * kCUs) p /= 2;
-  if (p < block_size) p = block_size;
-  return p - p % block_size;
+  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
+  int64_t p;
+  if (pairs <= kCUs) {
+    const int64_t np = kCUs / pairs;
+    p = (L + np - 1) / np;
+    if (p > pa::kMaxPartition) p = pa::kMaxPartition;
+  } else {
+    p = 1024;
+    while (p > 128 && pairs * ((L + p - 1) / p) < 2 * kCUs) p /= 2;
+  }
+  p = (p + block_size - 1) / block_size * block_size;
+  if (p > pa::kMaxPartition) p -= block_size;
+  return (int32_t)p;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -190,10 +202,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
   return ws_layout(num_seqs, num_heads, head_dim, ceil_div(max_seq_len, p)).bytes;
 }
 
-pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
-                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                       int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
-                       int32_t partition_size, hipStream_t stream) {
+static pa_status decode_call(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                             int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                             int32_t partition_size, int stage, hipEvent_t t0, hipEvent_t t1,
+                             hipStream_t stream) {
   const pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
@@ -220,6 +233,11 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, c
   a.scale = scale;
   a.partition = p;
   a.num_partitions = max_seq_len > 0 ? ceil_div(max_seq_len, p) : 1;
+  // 8-wave workgroups (one per compute unit) when the workgroups fit in one
+  // round of the chip, else 4-wave ones (two per compute unit).
+  a.waves = (int64_t)num_seqs * cache->num_kv_heads * a.num_partitions <= kCUs ? 8 : 4;
+  a.t0 = t0;
+  a.t1 = t1;
   if (max_seq_len > p) {
     const WsLayout wl = ws_layout(num_seqs, num_heads, cache->head_dim, a.num_partitions);
     if (!workspace || workspace_bytes < wl.bytes) return PA_ERR_WORKSPACE;
@@ -228,8 +246,34 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, c
     a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
     a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
   }
-  const hipError_t e = pa::launch_decode(a, stream);
+  const hipError_t e = pa::launch_decode(a, stage, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                       int32_t partition_size, hipStream_t stream) {
+  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
+                     scale, workspace, workspace_bytes, partition_size, 0, nullptr, nullptr, stream);
+}
+
+pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                          int32_t partition_size, hipEvent_t kernel_start, hipEvent_t kernel_stop,
+                          hipStream_t stream) {
+  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
+                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, stream);
+}
+
+pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                          int32_t partition_size, int32_t stage, hipStream_t stream) {
+  if (stage != 1 && stage != 2) return PA_ERR_SHAPE;
+  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
+                     scale, workspace, workspace_bytes, partition_size, stage, nullptr, nullptr, stream);
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,

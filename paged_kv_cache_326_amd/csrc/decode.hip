@@ -48,6 +48,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -55,7 +57,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kNW = 4;     // wavefronts per workgroup (two workgroups per CU at 2 waves per SIMD)
 constexpr int kStep = 32;  // tokens per step
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -112,23 +113,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
 
-// LDS of one workgroup: the partition's block-table slice, and per wave its
-// partial output [G][D], maximum and sum per head for the final merge.
+// LDS of one workgroup of NW waves: the partition's block-table slice, and
+// per wave its partial output [G][D], maximum and sum per head for the
+// final merge.
 struct SmemLayout {
   int bt_off, o_off, m_off, l_off, bytes;
 };
 
-__host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, int D) {
+__host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, int D, int NW) {
   SmemLayout s;
   int off = 0;
   s.bt_off = off;
   off += ((partition / B) * 4 + 15) & ~15;
   s.o_off = off;
-  off += kNW * G * D * 4;
+  off += NW * G * D * 4;
   s.m_off = off;
-  off += kNW * G * 4;
+  off += NW * G * 4;
   s.l_off = off;
-  off += kNW * G * 4;
+  off += NW * G * 4;
   s.bytes = off;
   return s;
 }
@@ -177,7 +179,7 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
   return den > 0.f ? num / den : 0.f;
 }
 
-template <typename T, int D, int B, int G>
+template <int kNW, typename T, int D, int B, int G>
 __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_partition_kernel(DecodeArgs a) {
   using QT = typename Dec<T>::Q;
@@ -193,16 +195,18 @@ decode_partition_kernel(DecodeArgs a) {
   static_assert(NLK >= 1 && QW >= 1 && B % 8 == 0 && G <= 16, "unsupported shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // 1-D grid, (sequence, KV head) fastest and partition slowest: workgroup
-  // ids are dealt to the 8 XCDs round-robin, so each XCD gets whole
-  // (sequence, KV head) pairs and short sequences spread over all XCDs.
+  // 1-D grid, (sequence, KV head) fastest and partition slowest, last
+  // partition first: workgroup ids are dealt to the 8 XCDs round-robin, so
+  // each XCD gets whole (sequence, KV head) pairs and short sequences spread
+  // over all XCDs; the late partitions exist only for long sequences, and
+  // starting them first keeps the longest chains of work off the tail.
   const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
-  const int part = blockIdx.x / (a.num_seqs * a.cache.num_kv_heads);
+  const int part = a.num_partitions - 1 - (int)(blockIdx.x / (a.num_seqs * a.cache.num_kv_heads));
   const int g = sg % a.cache.num_kv_heads;
   const int s = sg / a.cache.num_kv_heads;
   const int P = a.partition;
   const int nbp = P / B;
-  const SmemLayout lay = smem_layout(P, B, G, D);
+  const SmemLayout lay = smem_layout(P, B, G, D, kNW);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -214,9 +218,9 @@ decode_partition_kernel(DecodeArgs a) {
   const int tok0 = part * P;
   const int blk0 = tok0 / B;
 
-  // The table slice of the whole partition range is fetched without waiting
-  // for seq_len (it lies inside the table row either way), so the two loads
-  // overlap.
+  // The first NT entries of the partition's table slice are fetched without
+  // waiting for seq_len (they lie inside the table row either way), so the
+  // two loads overlap.
   int bt_id = -1;
   if (tid < nbp && blk0 + tid < a.max_blocks) bt_id = a.block_tables[(int64_t)s * a.max_blocks + blk0 + tid];
   int L = a.seq_lens[s];
@@ -237,6 +241,10 @@ decode_partition_kernel(DecodeArgs a) {
 
   // 1. Block-table slice -> LDS.  Entries outside the pool become -1.
   if (tid < nbp) s_bt[tid] = (bt_id < 0 || bt_id >= a.cache.num_blocks) ? -1 : bt_id;
+  for (int j = tid + NT; j < nbp; j += NT) {
+    const int id = blk0 + j < a.max_blocks ? a.block_tables[(int64_t)s * a.max_blocks + blk0 + j] : -1;
+    s_bt[j] = (id < 0 || id >= a.cache.num_blocks) ? -1 : id;
+  }
 
   // 2. Query operand: lane (head r, group grp) holds, for K load ls, the
   // query elements 4*CE*ls + CE*grp .. + CE-1 of head r (zero for r >= G).
@@ -514,64 +522,78 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
   store_elem<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
 }
 
-template <typename T, int D, int B, int G>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const SmemLayout lay = smem_layout(a.partition, B, G, D);
+// With events, the kernel's own start and end are recorded into them
+// (hipExtLaunchKernel): its execution time, with no packet of its own
+// between this launch and the next.
+template <int NW, typename T, int D, int B, int G>
+hipError_t launch_partitions(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const SmemLayout lay = smem_layout(a.partition, B, G, D, NW);
   dim3 grid((unsigned)((a.num_partitions > 0 ? a.num_partitions : 1) * a.cache.num_kv_heads * a.num_seqs));
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G>), grid, dim3(kNW * 64), lay.bytes, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.max_seq_len > a.partition) {
+  if (t0 || t1) {
+    hipExtLaunchKernelGGL((decode_partition_kernel<NW, T, D, B, G>), grid, dim3(NW * 64), (uint32_t)lay.bytes, stream,
+                          t0, t1, 0u, a);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<NW, T, D, B, G>), grid, dim3(NW * 64), lay.bytes, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// stage 1: partition kernel; stage 2: merge (only when some sequence can be
+// longer than one partition); 0: both.
+template <typename T, int D, int B, int G>
+hipError_t launch_typed(const DecodeArgs& a, int stage, hipStream_t stream) {
+  if (stage != 2) {
+    const hipError_t e = a.waves == 8 ? launch_partitions<8, T, D, B, G>(a, stream, a.t0, a.t1)
+                                      : launch_partitions<4, T, D, B, G>(a, stream, a.t0, a.t1);
+    if (e != hipSuccess) return e;
+  }
+  if (stage != 1 && a.max_seq_len > a.partition) {
     hipLaunchKernelGGL((decode_reduce_kernel<typename Dec<T>::Q, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
                        stream, a);
-    e = hipGetLastError();
+    return hipGetLastError();
   }
-  return e;
+  return hipSuccess;
 }
 
 template <typename T, int D, int B>
-hipError_t dispatch_g(const DecodeArgs& a, int G, hipStream_t stream) {
+hipError_t dispatch_g(const DecodeArgs& a, int G, int stage, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_typed<T, D, B, 1>(a, stream);
-    case 2: return launch_typed<T, D, B, 2>(a, stream);
-    case 4: return launch_typed<T, D, B, 4>(a, stream);
-    case 8: return launch_typed<T, D, B, 8>(a, stream);
+    case 1: return launch_typed<T, D, B, 1>(a, stage, stream);
+    case 2: return launch_typed<T, D, B, 2>(a, stage, stream);
+    case 4: return launch_typed<T, D, B, 4>(a, stage, stream);
+    case 8: return launch_typed<T, D, B, 8>(a, stage, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
-hipError_t dispatch_b(const DecodeArgs& a, int G, hipStream_t stream) {
+hipError_t dispatch_b(const DecodeArgs& a, int G, int stage, hipStream_t stream) {
   switch (a.cache.block_size) {
-    case 16: return dispatch_g<T, D, 16>(a, G, stream);
-    case 32: return dispatch_g<T, D, 32>(a, G, stream);
+    case 16: return dispatch_g<T, D, 16>(a, G, stage, stream);
+    case 32: return dispatch_g<T, D, 32>(a, G, stage, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t dispatch_d(const DecodeArgs& a, int G, hipStream_t stream) {
+hipError_t dispatch_d(const DecodeArgs& a, int G, int stage, hipStream_t stream) {
   switch (a.cache.head_dim) {
-    case 64: return dispatch_b<T, 64>(a, G, stream);
-    case 128: return dispatch_b<T, 128>(a, G, stream);
+    case 64: return dispatch_b<T, 64>(a, G, stage, stream);
+    case 128: return dispatch_b<T, 128>(a, G, stage, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t decode_smem_bytes(int partition, int block_size, int group, int head_dim) {
-  return (size_t)smem_layout(partition, block_size, group, head_dim).bytes;
-}
-
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int stage, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   const int G = a.num_heads / a.cache.num_kv_heads;
   switch (a.cache.dtype) {
-    case DType::kF32: return dispatch_d<float>(a, G, stream);
-    case DType::kF16: return dispatch_d<f16_t>(a, G, stream);
-    case DType::kBF16: return dispatch_d<bf16_t>(a, G, stream);
-    case DType::kFP8: return dispatch_d<fp8_t>(a, G, stream);
+    case DType::kF32: return dispatch_d<float>(a, G, stage, stream);
+    case DType::kF16: return dispatch_d<f16_t>(a, G, stage, stream);
+    case DType::kBF16: return dispatch_d<bf16_t>(a, G, stage, stream);
+    case DType::kFP8: return dispatch_d<fp8_t>(a, G, stage, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -29,6 +29,8 @@ struct DecodeArgs {
   float scale;
   int32_t partition;      // tokens per partition, multiple of block_size
   int32_t num_partitions; // ceil(max_seq_len / partition)
+  int32_t waves;          // wavefronts per partition workgroup: 4 or 8
+  hipEvent_t t0, t1;      // optional: the partition kernel's own start / end
   float* ws_m;            // [num_seqs][num_heads][num_partitions]
   float* ws_l;            // same
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]
@@ -47,7 +49,7 @@ struct PrefillArgs {
   float scale;
 };
 
-constexpr int kMaxPartition = 1024;
+constexpr int kMaxPartition = 4096;
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                                const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
@@ -65,7 +67,8 @@ hipError_t launch_append(const KvCacheArgs& c, const void* key, const void* valu
 hipError_t launch_block_move(const KvCacheArgs& c, const int32_t* src, const int32_t* dst, void* kbuf, void* vbuf,
                              int32_t n, int mode, hipStream_t stream);
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// stage 1: partition kernel; 2: merge of the partials; 0: both.
+hipError_t launch_decode(const DecodeArgs& a, int stage, hipStream_t stream);
 
 // Query positions one prefill workgroup covers for a head group of `group`.
 int prefill_positions_per_tile(int group);

@@ -58,6 +58,8 @@ EXPORTS = (
     "pa_decode_workspace_bytes",
     "pa_decode",
     "pa_decode_ex",
+    "pa_decode_stage",
+    "pa_decode_timed",
     "pa_prefill_chunk",
     "pa_copy_blocks",
     "pa_gather_blocks",
@@ -111,6 +113,10 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_ex.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp]
     L.pa_decode_ex.restype = ctypes.c_int
+    L.pa_decode_stage.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, i32, vp]
+    L.pa_decode_stage.restype = ctypes.c_int
+    L.pa_decode_timed.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp, vp, vp]
+    L.pa_decode_timed.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [cache_p, vp, vp, i32p, i32p, i32p, i32, i32, i32, i32, f32, vp]
     L.pa_prefill_chunk.restype = ctypes.c_int
     for name in ("pa_copy_blocks",):
@@ -287,7 +293,10 @@ def decode_workspace(query, key_cache, max_seq_len: int, partition_size: int = 0
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
-              workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None, scales=None):
+              workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None, scales=None,
+              stage: int = 0):
+    """Decode attention; ``stage`` 1 or 2 runs only the partition kernel or
+    only the merge (pa_decode_stage), 0 both (pa_decode_ex)."""
     c = kv_cache(key_cache, value_cache, scales)
     _need(query, "query", io_dtype(key_cache))
     _need(out, "out", io_dtype(key_cache))
@@ -300,10 +309,46 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale:
         workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().pa_decode_ex(ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-                            seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(), ws_bytes,
-                            int(partition_size), _stream(stream))
+    args = (ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+            seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(), ws_bytes, int(partition_size))
+    if stage:
+        st = lib().pa_decode_stage(*args, int(stage), _stream(stream))
+    else:
+        st = lib().pa_decode_ex(*args, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def _event_handle(ev) -> int:
+    """Raw HIP event of a torch.cuda.Event (which must have been recorded
+    once, so that it exists) or an integer handle."""
+    h = ev if isinstance(ev, int) else ev.cuda_event
+    if not h:
+        raise ValueError("record the event once before passing it (torch creates events lazily)")
+    return int(h)
+
+
+def pa_decode_timed(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                    kernel_start, kernel_stop, workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                    stream=None, scales=None):
+    """pa_decode whose partition kernel records its own start and end into
+    the two events (torch.cuda.Event or raw handles)."""
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = query.shape
+    if out.shape != query.shape or D != c.head_dim or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("shape mismatch between query/out/block_tables/seq_lens and the cache")
+    if workspace is None:
+        workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
+    _need(workspace, "workspace")
+    st = lib().pa_decode_timed(ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(),
+                               block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), int(partition_size),
+                               _event_handle(kernel_start), _event_handle(kernel_stop), _stream(stream))
+    _check(st, "pa_decode_timed")
     return out
 
 
