@@ -179,14 +179,27 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
   return den > 0.f ? num / den : 0.f;
 }
 
+// 8-wave workgroups (one per compute unit) keep two steps in flight per
+// wave at 2 waves per SIMD; 4-wave workgroups of 16-bit types keep one and
+// fit 3 waves per SIMD, i.e. three workgroups per compute unit, which serves
+// batches of many short or mixed-length sequences better (FP8 steps are
+// small enough to keep two either way; float32 is a correctness path).
+template <int kNW, typename T>
+struct WaveCfg {
+  static constexpr bool kThree = kNW == 4 && Elem<T>::kBytes <= 2;
+  static constexpr int kWavesPerEU = kThree ? 3 : 2;
+  static constexpr int kRing = kThree && Elem<T>::kBytes == 2 ? 1 : Dec<T>::NBUF;
+};
+
 template <int kNW, typename T, int D, int B, int G>
-__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(WaveCfg<kNW, T>::kWavesPerEU)))
 decode_partition_kernel(DecodeArgs a) {
   using QT = typename Dec<T>::Q;
   constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
   constexpr bool kF32 = std::is_same<T, float>::value;
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
-  constexpr int CE = Dec<T>::CE, KE = Dec<T>::KE, VW = Dec<T>::VW, NBUF = Dec<T>::NBUF;
+  constexpr int CE = Dec<T>::CE, KE = Dec<T>::KE, VW = Dec<T>::VW;
+  constexpr int NBUF = WaveCfg<kNW, T>::kRing;
   constexpr int NLK = D / (4 * CE);                 // K loads per lane per 16-token half
   constexpr int NSUB = CE / KE;                     // products per K load
   constexpr int QW = CE * (int)sizeof(QT) / 16;     // 16-byte query pieces per K load
