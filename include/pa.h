@@ -227,6 +227,23 @@ pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query
                           size_t workspace_bytes, int32_t partition_size, hipEvent_t kernel_start,
                           hipEvent_t kernel_stop, hipStream_t stream);
 
+/* One decode step in one call: every sequence's new token (position
+ * seq_lens[s] - 1, rows new_key / new_value [num_seqs][num_kv_heads]
+ * [head_dim] in the cache dtype, float16 for an FP8 pool) is written into
+ * its pool slot exactly as pa_append_kv writes a one-token step (the slot,
+ * or -1 when its block is missing from the table or the pool, goes to
+ * slot_mapping [num_seqs], int64), then decode attention runs as in
+ * pa_decode_timed.  The write is done by the partition workgroup that owns
+ * that position, so no separate scatter launch is needed.  seq_lens are
+ * clamped to max_seq_len for both parts.  Events may be NULL. */
+pa_status pa_decode_append(const pa_kv_cache* cache, const void* new_key, const void* new_value,
+                           int64_t* slot_mapping, void* out, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t max_seq_len, float scale, void* workspace,
+                           size_t workspace_bytes, int32_t partition_size, hipEvent_t kernel_start,
+                           hipEvent_t kernel_stop, hipStream_t stream);
+
 /* Chunked-prefill attention over the paged cache (causal).  [P1]
  * "工程边界与架构取舍": prefill is a compute-bound matrix product and a long
  * prompt is processed in chunks interleaved with decode steps; the chunk

@@ -206,7 +206,7 @@ static pa_status decode_call(const pa_kv_cache* cache, void* out, const void* qu
                              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                              int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                              int32_t partition_size, int stage, hipEvent_t t0, hipEvent_t t1,
-                             hipStream_t stream) {
+                             const void* new_key, const void* new_value, int64_t* slots, hipStream_t stream) {
   const pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
@@ -238,6 +238,9 @@ static pa_status decode_call(const pa_kv_cache* cache, void* out, const void* qu
   a.waves = (int64_t)num_seqs * cache->num_kv_heads * a.num_partitions <= kCUs ? 8 : 4;
   a.t0 = t0;
   a.t1 = t1;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.slots = slots;
   if (max_seq_len > p) {
     const WsLayout wl = ws_layout(num_seqs, num_heads, cache->head_dim, a.num_partitions);
     if (!workspace || workspace_bytes < wl.bytes) return PA_ERR_WORKSPACE;
@@ -255,7 +258,8 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, c
                        int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                        int32_t partition_size, hipStream_t stream) {
   return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, 0, nullptr, nullptr, stream);
+                     scale, workspace, workspace_bytes, partition_size, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     stream);
 }
 
 pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -264,7 +268,8 @@ pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query
                           int32_t partition_size, hipEvent_t kernel_start, hipEvent_t kernel_stop,
                           hipStream_t stream) {
   return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, stream);
+                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, nullptr, nullptr,
+                     nullptr, stream);
 }
 
 pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -273,7 +278,8 @@ pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query
                           int32_t partition_size, int32_t stage, hipStream_t stream) {
   if (stage != 1 && stage != 2) return PA_ERR_SHAPE;
   return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, stage, nullptr, nullptr, stream);
+                     scale, workspace, workspace_bytes, partition_size, stage, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, stream);
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -310,6 +316,18 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* quer
   a.scale = scale;
   const hipError_t e = pa::launch_prefill(a, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode_append(const pa_kv_cache* cache, const void* new_key, const void* new_value,
+                           int64_t* slot_mapping, void* out, const void* query, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                           int32_t partition_size, hipEvent_t kernel_start, hipEvent_t kernel_stop,
+                           hipStream_t stream) {
+  if (num_seqs > 0 && (!new_key || !new_value || !slot_mapping)) return PA_ERR_NULL;
+  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
+                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, new_key,
+                     new_value, slot_mapping, stream);
 }
 
 }  // extern "C"

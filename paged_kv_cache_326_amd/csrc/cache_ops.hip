@@ -34,82 +34,6 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(
   }
 }
 
-// New K/V rows are stored as they come, except into an FP8 pool, whose rows
-// arrive as float16 and are quantised on the way: code = E4M3(x / scale),
-// the division in float32 (IEEE, rounded to nearest).
-template <typename T>
-struct Src {
-  using type = T;
-};
-template <>
-struct Src<fp8_t> {
-  using type = f16_t;
-};
-
-// Store the VEC = vec16<Src<T>> source elements of one 16-byte chunk.
-template <typename T>
-__device__ __forceinline__ void store_chunk(T* dst, const u32x4& data, float) {
-  *reinterpret_cast<u32x4*>(dst) = data;
-}
-template <>
-__device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4& data, float scale) {
-  uint32_t w[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t word = data[2 * i + j];
-      const uint32_t lo = f32_to_e4m3(f16_lo(word) / scale);
-      const uint32_t hi = f32_to_e4m3(f16_hi(word) / scale);
-      acc |= (lo | (hi << 8)) << (16 * j);
-    }
-    w[i] = acc;
-  }
-  *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-}
-
-// Store the same chunk as one column piece of a transposed value tile:
-// element e goes to p[e * stride].
-template <typename T>
-__device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4& data, float scale) {
-  if constexpr (Elem<T>::kBytes == 4) {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[e * stride] = data[e];
-  } else if constexpr (Elem<T>::kBytes == 2) {
-    uint16_t* q = reinterpret_cast<uint16_t*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t word = data[e / 2];
-      q[e * stride] = (uint16_t)(word >> (16 * (e % 2)));
-    }
-  } else {
-    uint8_t* q = reinterpret_cast<uint8_t*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t word = data[e / 2];
-      const float x = e % 2 ? f16_hi(word) : f16_lo(word);
-      q[e * stride] = (uint8_t)f32_to_e4m3(x / scale);
-    }
-  }
-}
-
-// The destination of one 16-byte source chunk (dims ch*VEC ..) of token
-// slot (blk, off), KV head h: a key row piece, or a value column piece.
-template <typename T>
-__device__ __forceinline__ void store_kv_chunk(T* key_cache, T* value_cache, int which, int64_t blk, int off, int h,
-                                               int ch, int vec, int num_kv_heads, int head_dim, int block_size,
-                                               const u32x4& data, float k_scale, float v_scale) {
-  if (which == 0) {
-    T* dst = key_cache + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * vec;
-    store_chunk<T>(dst, data, k_scale);
-  } else {
-    T* dst = value_cache + ((blk * num_kv_heads + h) * head_dim + ch * vec) * block_size + off;
-    store_column<T>(dst, block_size, data, v_scale);
-  }
-}
-
 // Each thread moves one 16-byte chunk of one token's K or V row.  A token row
 // of one KV head is head_dim elements.  The key tile of (block, KV head) is
 // [block_size][head_dim] (the row lands at

@@ -273,6 +273,31 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();  // table slice visible
 
+  // Fused append: in the workgroup whose partition holds the sequence's last
+  // position, the wave that will process the partition's last step writes
+  // this step's token (KV head g) into its slot, exactly as the scatter
+  // does, and waits until its stores have completed before it issues any
+  // load; no other wave reads that token's block (the last block belongs to
+  // the last step only), so the other waves start streaming at once.
+  const int nsteps = (ntok + kStep - 1) / kStep;
+  if (a.new_key != nullptr && ntok > 0 && tok0 + ntok == L && w == (nsteps - 1) % kNW) {
+    using S = typename Src<T>::type;
+    constexpr int VS = vec16<S>();
+    constexpr int NCH = D / VS;  // 16-byte source chunks per row
+    static_assert(2 * NCH <= 64, "one wave writes the token");
+    const int pb = s_bt[(ntok - 1) / B];
+    const int off = (L - 1) % B;
+    if (lane < 2 * NCH && pb >= 0) {
+      const int which = lane / NCH, c = lane % NCH;
+      const S* src = reinterpret_cast<const S*>(which ? a.new_value : a.new_key) + ((int64_t)s * Hkv + g) * D + c * VS;
+      store_kv_chunk<T>(reinterpret_cast<T*>(a.cache.key_cache), reinterpret_cast<T*>(a.cache.value_cache), which, pb,
+                        off, g, c, VS, Hkv, D, B, *reinterpret_cast<const u32x4*>(src), a.cache.k_scale,
+                        a.cache.v_scale);
+    }
+    if (lane == 0 && g == 0) a.slots[s] = pb >= 0 ? (int64_t)pb * B + off : -1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
   const int64_t blk_stride = (int64_t)Hkv * B * D;
   const T* kbase = reinterpret_cast<const T*>(a.cache.key_cache) + (int64_t)g * B * D;
   const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * D * B;
@@ -453,7 +478,6 @@ decode_partition_kernel(DecodeArgs a) {
   };
 
   // 3. The wave's steps w, w + kNW, ..., NBUF of them in flight.
-  const int nsteps = (ntok + kStep - 1) / kStep;
   const int nmine = nsteps > w ? (nsteps - w + kNW - 1) / kNW : 0;
   Buf buf[NBUF];
 #pragma unroll

@@ -31,6 +31,12 @@ struct DecodeArgs {
   int32_t num_partitions; // ceil(max_seq_len / partition)
   int32_t waves;          // wavefronts per partition workgroup: 4 or 8
   hipEvent_t t0, t1;      // optional: the partition kernel's own start / end
+  // Optional fused append: token seq_lens[s]-1 of every sequence, rows
+  // [num_seqs][num_kv_heads][head_dim] (float16 for an FP8 pool), is written
+  // into its pool slot first; slots[s] receives the slot or -1.
+  const void* new_key;
+  const void* new_value;
+  int64_t* slots;
   float* ws_m;            // [num_seqs][num_heads][num_partitions]
   float* ws_l;            // same
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]

@@ -60,6 +60,7 @@ EXPORTS = (
     "pa_decode_ex",
     "pa_decode_stage",
     "pa_decode_timed",
+    "pa_decode_append",
     "pa_prefill_chunk",
     "pa_copy_blocks",
     "pa_gather_blocks",
@@ -117,6 +118,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_stage.restype = ctypes.c_int
     L.pa_decode_timed.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp, vp, vp]
     L.pa_decode_timed.restype = ctypes.c_int
+    L.pa_decode_append.argtypes = [cache_p, vp, vp, i64p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp, vp,
+                                   vp]
+    L.pa_decode_append.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [cache_p, vp, vp, i32p, i32p, i32p, i32, i32, i32, i32, f32, vp]
     L.pa_prefill_chunk.restype = ctypes.c_int
     for name in ("pa_copy_blocks",):
@@ -350,6 +354,40 @@ def pa_decode_timed(out, query, key_cache, value_cache, block_tables, seq_lens, 
                                _event_handle(kernel_start), _event_handle(kernel_stop), _stream(stream))
     _check(st, "pa_decode_timed")
     return out
+
+
+def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, scale: float,
+                     max_seq_len: int, slot_mapping=None, workspace: Optional[torch.Tensor] = None,
+                     partition_size: int = 0, kernel_start=None, kernel_stop=None, stream=None, scales=None):
+    """One decode step: each sequence's new token (position seq_lens[s]-1)
+    written into the pool, then decode attention, in the partition kernel."""
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
+    _need(new_key, "new_key", io_dtype(key_cache))
+    _need(new_value, "new_value", io_dtype(key_cache))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = query.shape
+    if out.shape != query.shape or D != c.head_dim or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("shape mismatch between query/out/block_tables/seq_lens and the cache")
+    if new_key.shape != (S, c.num_kv_heads, D) or new_value.shape != new_key.shape:
+        raise ValueError("new_key/new_value must be [num_seqs, num_kv_heads, head_dim]")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(S, dtype=torch.int64, device=query.device)
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    if workspace is None:
+        workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
+    _need(workspace, "workspace")
+    ev0 = None if kernel_start is None else _event_handle(kernel_start)
+    ev1 = None if kernel_stop is None else _event_handle(kernel_stop)
+    st = lib().pa_decode_append(ctypes.byref(c), new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(),
+                                out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+                                seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), int(partition_size), ev0, ev1,
+                                _stream(stream))
+    _check(st, "pa_decode_append")
+    return slot_mapping
 
 
 def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, block_tables, scale: float,

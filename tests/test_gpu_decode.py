@@ -178,6 +178,30 @@ def test_decode_timed_matches_and_times_the_partition_kernel():
     assert 0.0 < ms < 100.0
 
 
+@pytest.mark.parametrize("k,partition", [(1, 0), (2, 0), (2, 512), (3, 0), (3, 64), (4, 0)])
+def test_fused_append_decode_matches_append_then_decode(k, partition):
+    # One call (the partition kernel writes each sequence's new token) against
+    # pa_append_kv followed by pa_decode: the same pool bytes, slots and
+    # outputs, bit for bit; and the output against the oracle.
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    w = synth.config(k, scale_down=4 if k in (2, 3) else 1)
+    ref_w = harness.GpuWorkload(w)
+    ref_w.append()
+    ref_out = ref_w.decode(partition_size=partition).clone()
+    gw = harness.GpuWorkload(w)
+    slots = torch.full((w.num_seqs,), -7, dtype=torch.int64, device="cuda")
+    pa.pa_decode_append(gw.out, gw.query, gw.key_cache, gw.value_cache, gw.new_key, gw.new_value, gw.block_tables,
+                        gw.seq_lens, w.scale, w.max_seq_len, slot_mapping=slots, partition_size=partition)
+    _sync()
+    assert torch.equal(slots, ref_w.slot_mapping)
+    for a_, b_ in ((gw.key_cache, ref_w.key_cache), (gw.value_cache, ref_w.value_cache), (gw.out, ref_out)):
+        assert np.array_equal(harness.from_device(a_, w.dtype).view(np.uint8), harness.from_device(b_, w.dtype).view(np.uint8))
+    _, _, _, ref = harness.oracle_step(w)
+    _assert_close(_as64(gw.out, w.dtype), ref, w.dtype, f"fused append + decode, config {k}")
+
+
 @pytest.mark.parametrize("partition", [16, 32, 0])
 def test_decode_tiny_config_partitions(partition):
     w = synth.config(1)
