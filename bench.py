@@ -184,6 +184,17 @@ def secondary(copies_n: int):
         cs = _copies(w, copies_n)
         ws = [pa.decode_workspace(c.query, c.key_cache, w.max_seq_len) for c in cs]
         t = _median_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
+        # The same batch with the host plan (only partitions that hold tokens,
+        # longest first), as a scheduler that knows the lengths would call it.
+        Pk = pa.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, w.max_seq_len, w.block_size)
+        work = pa.decode_plan(w.seq_lens, w.max_seq_len, Pk)
+
+        def planned(i):
+            c = cs[i % len(cs)]
+            pa.pa_decode_run(c.out, c.query, c.key_cache, c.value_cache, c.block_tables, c.seq_lens, w.scale,
+                             w.max_seq_len, workspace=ws[i % len(cs)], partition_size=Pk, work=work)
+
+        tp = _median_us(planned)
         nb = algorithmic_decode_bytes(w)
         uniq = int((w.refcounts > 0).sum()) * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes * 2
         res[synth.CONFIG_NAMES[k]] = {
@@ -191,6 +202,9 @@ def secondary(copies_n: int):
             "frac_of_hbm_peak": round(nb / t / 1e3 / HBM_PEAK_GBS, 4),
             "attended_tokens_per_s": int(w.seq_lens.sum()) / (t * 1e-6),
             "unique_kv_bytes": uniq, "dtype": w.dtype,
+            "planned_decode_us": round(tp, 2), "planned_GBps": round(nb / tp / 1e3, 1),
+            "planned_frac_of_hbm_peak": round(nb / tp / 1e3 / HBM_PEAK_GBS, 4),
+            "planned_units": int(work.numel()),
         }
         del cs, ws
         torch.cuda.empty_cache()

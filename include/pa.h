@@ -244,6 +244,60 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* new_key, const 
                            size_t workspace_bytes, int32_t partition_size, hipEvent_t kernel_start,
                            hipEvent_t kernel_stop, hipStream_t stream);
 
+/* All decode options in one call.  Fields as in pa_decode_ex; the optional
+ * ones are NULL / 0 when unused:
+ *   stage            0 both launches, 1 the partition kernel, 2 the merge
+ *   new_key, new_value, slot_mapping   the fused append of pa_decode_append
+ *                    (all three or none)
+ *   work, num_work   a plan from pa_decode_plan for the same seq_lens,
+ *                    max_seq_len and partition_size (uploaded to device
+ *                    memory): only the listed partitions are launched, in
+ *                    that order, and the merge reads only the partitions
+ *                    each sequence has.  Without a plan the grid covers
+ *                    ceil(max_seq_len / partition) partitions of every
+ *                    sequence and empty ones exit at once.
+ *   kernel_start, kernel_stop   events that the partition kernel records
+ *                    its own start and end into
+ */
+typedef struct {
+  const pa_kv_cache* cache;
+  void* out;
+  const void* query;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t max_seq_len;
+  float scale;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t partition_size;
+  int32_t stage;
+  const void* new_key;
+  const void* new_value;
+  int64_t* slot_mapping;
+  const int32_t* work;
+  int32_t num_work;
+  hipEvent_t kernel_start;
+  hipEvent_t kernel_stop;
+} pa_decode_args;
+
+pa_status pa_decode_run(const pa_decode_args* args, hipStream_t stream);
+
+/* Host-side work list for decode batches of mixed lengths (no device
+ * memory; the caller's scheduler knows the lengths).  Lists, for the host
+ * copy of seq_lens (clamped to [0, max_seq_len]), every partition that
+ * holds a token (and partition 0 of empty sequences, which writes their
+ * zeros), longest first -- full partitions in sequence order, then the
+ * last partial ones by decreasing length -- each as
+ * sequence * ceil(max_seq_len / partition_size) + partition.  Writes the
+ * list only if capacity suffices; returns its length, or -1 on bad
+ * arguments.  partition_size must be the one the decode call uses (e.g.
+ * pa_decode_auto_partition's). */
+int32_t pa_decode_plan(const int32_t* seq_lens_host, int32_t num_seqs, int32_t max_seq_len,
+                       int32_t partition_size, int32_t* work, int32_t capacity);
+
 /* Chunked-prefill attention over the paged cache (causal).  [P1]
  * "工程边界与架构取舍": prefill is a compute-bound matrix product and a long
  * prompt is processed in chunks interleaved with decode steps; the chunk

@@ -1,6 +1,10 @@
 // C ABI of libpa.so: host-side argument checks, partition choice, workspace
 // layout and dispatch to the gfx950 kernels.  Every check runs before any
 // launch; a failed check launches nothing.
+#include <algorithm>
+#include <climits>
+#include <vector>
+
 #include "../../include/pa.h"
 #include "pa_launch.h"
 
@@ -202,64 +206,116 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
   return ws_layout(num_seqs, num_heads, head_dim, ceil_div(max_seq_len, p)).bytes;
 }
 
-static pa_status decode_call(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
-                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                             int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
-                             int32_t partition_size, int stage, hipEvent_t t0, hipEvent_t t1,
-                             const void* new_key, const void* new_value, int64_t* slots, hipStream_t stream) {
+static pa_status decode_run(const pa_decode_args* d, hipStream_t stream) {
+  if (!d) return PA_ERR_NULL;
+  const pa_kv_cache* cache = d->cache;
   const pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
-  if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (d->stage < 0 || d->stage > 2) return PA_ERR_SHAPE;
+  const int32_t num_seqs = d->num_seqs, num_heads = d->num_heads, max_seq_len = d->max_seq_len;
+  if (num_seqs < 0 || max_seq_len < 0 || d->max_blocks_per_seq <= 0 || d->num_work < 0) return PA_ERR_SHAPE;
   if (!supported_group(num_heads, cache->num_kv_heads)) {
     return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
   }
-  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
-  int p = partition_size;
+  if ((int64_t)max_seq_len > (int64_t)d->max_blocks_per_seq * cache->block_size) return PA_ERR_SHAPE;
+  int p = d->partition_size;
   if (p == 0) p = pa_decode_auto_partition(num_seqs, cache->num_kv_heads, max_seq_len, cache->block_size);
   if (p <= 0 || p % cache->block_size || p > pa::kMaxPartition) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !query || !block_tables || !seq_lens) return PA_ERR_NULL;
+  if (!d->out || !d->query || !d->block_tables || !d->seq_lens) return PA_ERR_NULL;
+  const bool append = d->new_key || d->new_value || d->slot_mapping;
+  if (append && (!d->new_key || !d->new_value || !d->slot_mapping)) return PA_ERR_NULL;
+  if (d->work && d->num_work == 0) return PA_ERR_SHAPE;  // a plan always holds partition 0 of every sequence
 
   pa::DecodeArgs a{};
   a.cache = to_args(cache);
-  a.out = out;
-  a.query = query;
-  a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  a.seq_lens = seq_lens;
+  a.out = d->out;
+  a.query = d->query;
+  a.block_tables = d->block_tables;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.seq_lens = d->seq_lens;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.max_seq_len = max_seq_len;
-  a.scale = scale;
+  a.scale = d->scale;
   a.partition = p;
   a.num_partitions = max_seq_len > 0 ? ceil_div(max_seq_len, p) : 1;
+  a.work = d->work;
+  a.num_work = d->work ? d->num_work : 0;
   // 8-wave workgroups (one per compute unit) when the workgroups fit in one
-  // round of the chip, else 4-wave ones (two per compute unit).
-  a.waves = (int64_t)num_seqs * cache->num_kv_heads * a.num_partitions <= kCUs ? 8 : 4;
-  a.t0 = t0;
-  a.t1 = t1;
-  a.new_key = new_key;
-  a.new_value = new_value;
-  a.slots = slots;
+  // round of the chip, else 4-wave ones (three per compute unit).
+  const int64_t units = d->work ? (int64_t)d->num_work : (int64_t)num_seqs * a.num_partitions;
+  a.waves = units * cache->num_kv_heads <= kCUs ? 8 : 4;
+  a.t0 = d->kernel_start;
+  a.t1 = d->kernel_stop;
+  a.new_key = d->new_key;
+  a.new_value = d->new_value;
+  a.slots = d->slot_mapping;
   if (max_seq_len > p) {
     const WsLayout wl = ws_layout(num_seqs, num_heads, cache->head_dim, a.num_partitions);
-    if (!workspace || workspace_bytes < wl.bytes) return PA_ERR_WORKSPACE;
-    char* base = static_cast<char*>(workspace);
+    if (!d->workspace || d->workspace_bytes < wl.bytes) return PA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(d->workspace);
     a.ws_m = reinterpret_cast<float*>(base + wl.m_off);
     a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
     a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
   }
-  const hipError_t e = pa::launch_decode(a, stage, stream);
+  const hipError_t e = pa::launch_decode(a, d->stage, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+static pa_decode_args basic_args(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t max_seq_len, float scale, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_size) {
+  pa_decode_args d{};
+  d.cache = cache;
+  d.out = out;
+  d.query = query;
+  d.block_tables = block_tables;
+  d.max_blocks_per_seq = max_blocks_per_seq;
+  d.seq_lens = seq_lens;
+  d.num_seqs = num_seqs;
+  d.num_heads = num_heads;
+  d.max_seq_len = max_seq_len;
+  d.scale = scale;
+  d.workspace = workspace;
+  d.workspace_bytes = workspace_bytes;
+  d.partition_size = partition_size;
+  return d;
+}
+
+pa_status pa_decode_run(const pa_decode_args* args, hipStream_t stream) { return decode_run(args, stream); }
+
+int32_t pa_decode_plan(const int32_t* seq_lens_host, int32_t num_seqs, int32_t max_seq_len, int32_t partition_size,
+                       int32_t* work, int32_t capacity) {
+  if (num_seqs < 0 || max_seq_len < 0 || partition_size <= 0 || (num_seqs > 0 && !seq_lens_host)) return -1;
+  const int64_t P = partition_size;
+  const int64_t np = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
+  struct Unit {
+    int64_t size, s, part;
+  };
+  std::vector<Unit> units;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int64_t L = seq_lens_host[s];
+    L = L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+    const int64_t parts = L > 0 ? (L + P - 1) / P : 1;  // partition 0 even when empty: it writes the zeros
+    for (int64_t q = 0; q < parts; ++q) units.push_back({std::min(P, L - q * P), s, q});
+  }
+  if (units.size() > (size_t)INT32_MAX / 2 || (int64_t)num_seqs * np > INT32_MAX) return -1;
+  std::stable_sort(units.begin(), units.end(), [](const Unit& x, const Unit& y) { return x.size > y.size; });
+  const int32_t n = (int32_t)units.size();
+  if (work && capacity >= n)
+    for (int32_t k = 0; k < n; ++k) work[k] = (int32_t)(units[k].s * np + units[k].part);
+  return n;
 }
 
 pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                        int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                        int32_t partition_size, hipStream_t stream) {
-  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     stream);
+  const pa_decode_args d = basic_args(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                                      num_heads, max_seq_len, scale, workspace, workspace_bytes, partition_size);
+  return decode_run(&d, stream);
 }
 
 pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -267,9 +323,11 @@ pa_status pa_decode_timed(const pa_kv_cache* cache, void* out, const void* query
                           int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                           int32_t partition_size, hipEvent_t kernel_start, hipEvent_t kernel_stop,
                           hipStream_t stream) {
-  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, nullptr, nullptr,
-                     nullptr, stream);
+  pa_decode_args d = basic_args(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads,
+                                max_seq_len, scale, workspace, workspace_bytes, partition_size);
+  d.kernel_start = kernel_start;
+  d.kernel_stop = kernel_stop;
+  return decode_run(&d, stream);
 }
 
 pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -277,9 +335,10 @@ pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query
                           int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                           int32_t partition_size, int32_t stage, hipStream_t stream) {
   if (stage != 1 && stage != 2) return PA_ERR_SHAPE;
-  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, stage, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, stream);
+  pa_decode_args d = basic_args(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads,
+                                max_seq_len, scale, workspace, workspace_bytes, partition_size);
+  d.stage = stage;
+  return decode_run(&d, stream);
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
@@ -325,9 +384,14 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* new_key, const 
                            int32_t partition_size, hipEvent_t kernel_start, hipEvent_t kernel_stop,
                            hipStream_t stream) {
   if (num_seqs > 0 && (!new_key || !new_value || !slot_mapping)) return PA_ERR_NULL;
-  return decode_call(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads, max_seq_len,
-                     scale, workspace, workspace_bytes, partition_size, 0, kernel_start, kernel_stop, new_key,
-                     new_value, slot_mapping, stream);
+  pa_decode_args d = basic_args(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads,
+                                max_seq_len, scale, workspace, workspace_bytes, partition_size);
+  d.kernel_start = kernel_start;
+  d.kernel_stop = kernel_stop;
+  d.new_key = new_key;
+  d.new_value = new_value;
+  d.slot_mapping = slot_mapping;
+  return decode_run(&d, stream);
 }
 
 }  // extern "C"

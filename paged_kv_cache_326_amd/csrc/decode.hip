@@ -142,10 +142,10 @@ __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, i
 // all issued before any is used; batches combine with a running rescale.
 constexpr int kMergeBatch = 16;
 
+// np partitions of the sequence are merged; rows are num_partitions apart.
 template <int D>
-__device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d) {
-  const int np = a.num_partitions;
-  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * np;
+__device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
+  const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
   float M = -INFINITY, num = 0.f, den = 0.f;
   for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
@@ -213,10 +213,23 @@ decode_partition_kernel(DecodeArgs a) {
   // each XCD gets whole (sequence, KV head) pairs and short sequences spread
   // over all XCDs; the late partitions exist only for long sequences, and
   // starting them first keeps the longest chains of work off the tail.
-  const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
-  const int part = a.num_partitions - 1 - (int)(blockIdx.x / (a.num_seqs * a.cache.num_kv_heads));
-  const int g = sg % a.cache.num_kv_heads;
-  const int s = sg / a.cache.num_kv_heads;
+  // With a plan, workgroup i serves KV head i % H_kv of the listed unit
+  // i / H_kv (a sequence's partition), so the heads of a unit spread over
+  // the XCDs.
+  int s, g, part;
+  if (a.work) {
+    const int unit = blockIdx.x / a.cache.num_kv_heads;
+    g = blockIdx.x % a.cache.num_kv_heads;
+    const int wi = unit < a.num_work ? a.work[unit] : -1;
+    if (wi < 0 || wi >= a.num_seqs * a.num_partitions) return;  // not a unit of this call
+    s = wi / a.num_partitions;
+    part = wi % a.num_partitions;
+  } else {
+    const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
+    part = a.num_partitions - 1 - (int)(blockIdx.x / (a.num_seqs * a.cache.num_kv_heads));
+    g = sg % a.cache.num_kv_heads;
+    s = sg / a.cache.num_kv_heads;
+  }
   const int P = a.partition;
   const int nbp = P / B;
   const SmemLayout lay = smem_layout(P, B, G, D, kNW);
@@ -552,9 +565,13 @@ decode_partition_kernel(DecodeArgs a) {
 template <typename T, int D>
 __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
   const int s = blockIdx.y, hq = blockIdx.x, d = threadIdx.x;
-  int L = a.seq_lens[s];  // independent of the partial loads below
-  const float v = merge_partials<D>(a, s, hq, d);
+  int L = a.seq_lens[s];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  // Without a plan every partition wrote its partials or an m = -inf marker,
+  // so the loads need not wait for seq_len; with one, only the sequence's
+  // own partitions ran.
+  const int np = a.work ? (L + a.partition - 1) / a.partition : a.num_partitions;
+  const float v = merge_partials<D>(a, s, hq, d, np);
   if (L <= a.partition) return;  // written directly by the partition kernel
   store_elem<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
 }
@@ -565,7 +582,8 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
 template <int NW, typename T, int D, int B, int G>
 hipError_t launch_partitions(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const SmemLayout lay = smem_layout(a.partition, B, G, D, NW);
-  dim3 grid((unsigned)((a.num_partitions > 0 ? a.num_partitions : 1) * a.cache.num_kv_heads * a.num_seqs));
+  dim3 grid((unsigned)((a.work ? a.num_work : (a.num_partitions > 0 ? a.num_partitions : 1) * a.num_seqs) *
+                       a.cache.num_kv_heads));
   if (t0 || t1) {
     hipExtLaunchKernelGGL((decode_partition_kernel<NW, T, D, B, G>), grid, dim3(NW * 64), (uint32_t)lay.bytes, stream,
                           t0, t1, 0u, a);

@@ -37,6 +37,10 @@ struct DecodeArgs {
   const void* new_key;
   const void* new_value;
   int64_t* slots;
+  // Optional plan: work[i] = sequence * num_partitions + partition for the
+  // num_work launched units (else the grid covers every partition).
+  const int32_t* work;
+  int32_t num_work;
   float* ws_m;            // [num_seqs][num_heads][num_partitions]
   float* ws_l;            // same
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]

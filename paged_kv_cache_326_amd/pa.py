@@ -48,6 +48,32 @@ class pa_kv_cache(ctypes.Structure):
     ]
 
 
+class pa_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("cache", ctypes.POINTER(pa_kv_cache)),
+        ("out", ctypes.c_void_p),
+        ("query", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("partition_size", ctypes.c_int32),
+        ("stage", ctypes.c_int32),
+        ("new_key", ctypes.c_void_p),
+        ("new_value", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p),
+        ("work", ctypes.c_void_p),
+        ("num_work", ctypes.c_int32),
+        ("kernel_start", ctypes.c_void_p),
+        ("kernel_stop", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 EXPORTS = (
@@ -61,6 +87,8 @@ EXPORTS = (
     "pa_decode_stage",
     "pa_decode_timed",
     "pa_decode_append",
+    "pa_decode_run",
+    "pa_decode_plan",
     "pa_prefill_chunk",
     "pa_copy_blocks",
     "pa_gather_blocks",
@@ -121,6 +149,10 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.argtypes = [cache_p, vp, vp, i64p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp, vp,
                                    vp]
     L.pa_decode_append.restype = ctypes.c_int
+    L.pa_decode_run.argtypes = [ctypes.POINTER(pa_decode_args), vp]
+    L.pa_decode_run.restype = ctypes.c_int
+    L.pa_decode_plan.argtypes = [vp, i32, i32, i32, vp, i32]
+    L.pa_decode_plan.restype = i32
     L.pa_prefill_chunk.argtypes = [cache_p, vp, vp, i32p, i32p, i32p, i32, i32, i32, i32, f32, vp]
     L.pa_prefill_chunk.restype = ctypes.c_int
     for name in ("pa_copy_blocks",):
@@ -388,6 +420,62 @@ def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, blo
                                 _stream(stream))
     _check(st, "pa_decode_append")
     return slot_mapping
+
+
+def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int, device="cuda") -> torch.Tensor:
+    """pa_decode_plan on a host copy of seq_lens; the list, uploaded."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    L = lib()
+    n = L.pa_decode_plan(lens.ctypes.data, len(lens), int(max_seq_len), int(partition_size), None, 0)
+    if n < 0:
+        raise ValueError("pa_decode_plan rejected its arguments")
+    work = np.empty(max(n, 1), dtype=np.int32)
+    L.pa_decode_plan(lens.ctypes.data, len(lens), int(max_seq_len), int(partition_size), work.ctypes.data, n)
+    return torch.from_numpy(work[:n]).to(device)
+
+
+def pa_decode_run(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                  workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stage: int = 0,
+                  new_key=None, new_value=None, slot_mapping=None, work: Optional[torch.Tensor] = None,
+                  kernel_start=None, kernel_stop=None, stream=None, scales=None):
+    """Every decode option in one call (pa_decode_run)."""
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = query.shape
+    if out.shape != query.shape or D != c.head_dim or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("shape mismatch between query/out/block_tables/seq_lens and the cache")
+    if workspace is None:
+        workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
+    _need(workspace, "workspace")
+    d = pa_decode_args()
+    d.cache = ctypes.pointer(c)
+    d.out, d.query = out.data_ptr(), query.data_ptr()
+    d.block_tables, d.max_blocks_per_seq = block_tables.data_ptr(), block_tables.shape[1]
+    d.seq_lens, d.num_seqs, d.num_heads, d.max_seq_len = seq_lens.data_ptr(), S, Hq, int(max_seq_len)
+    d.scale = float(scale)
+    d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    d.partition_size, d.stage = int(partition_size), int(stage)
+    if new_key is not None:
+        _need(new_key, "new_key", io_dtype(key_cache))
+        _need(new_value, "new_value", io_dtype(key_cache))
+        _need(slot_mapping, "slot_mapping", torch.int64)
+        if new_key.shape != (S, c.num_kv_heads, D) or new_value.shape != new_key.shape or slot_mapping.shape != (S,):
+            raise ValueError("new_key/new_value [num_seqs, num_kv_heads, head_dim], slot_mapping [num_seqs]")
+        d.new_key, d.new_value, d.slot_mapping = new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr()
+    if work is not None:
+        _need(work, "work", torch.int32)
+        d.work, d.num_work = work.data_ptr(), work.numel()
+    if kernel_start is not None:
+        d.kernel_start = _event_handle(kernel_start)
+    if kernel_stop is not None:
+        d.kernel_stop = _event_handle(kernel_stop)
+    _check(lib().pa_decode_run(ctypes.byref(d), _stream(stream)), "pa_decode_run")
+    return out
 
 
 def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, block_tables, scale: float,

@@ -127,3 +127,66 @@ def test_decode_stage_argument_errors(L):
     assert L.pa_decode_stage(*args, 0, None) == 2
     c0 = _cache(pa, key_cache=0)
     assert L.pa_decode_stage(ctypes.byref(c0), *args[1:], 1, None) == 1
+
+
+def _plan(L, lens, maxL, P):
+    import numpy as np
+
+    arr = np.ascontiguousarray(lens, dtype=np.int32)
+    n = L.pa_decode_plan(arr.ctypes.data, len(arr), maxL, P, None, 0)
+    out = np.zeros(max(n, 1), np.int32)
+    assert L.pa_decode_plan(arr.ctypes.data, len(arr), maxL, P, out.ctypes.data, n) == n
+    return n, out[:n]
+
+
+def test_decode_plan_lists_live_partitions_longest_first(L):
+    import numpy as np
+
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        S = int(rng.integers(1, 40))
+        maxL = int(rng.integers(1, 5000))
+        P = int(rng.choice([16, 64, 256, 1024]))
+        lens = rng.integers(-3, maxL + 50, size=S)
+        n, work = _plan(L, lens, maxL, P)
+        np_ = -(-maxL // P)
+        # brute force: every (s, part) with a token, plus partition 0 of empty sequences
+        units = []
+        for s, l in enumerate(lens):
+            l = min(max(int(l), 0), maxL)
+            parts = -(-l // P) if l > 0 else 1
+            units += [(min(P, l - q * P), s, q) for q in range(parts)]
+        assert n == len(units)
+        got = [(int(x) // np_, int(x) % np_) for x in work]
+        assert sorted(got) == sorted((s, q) for _, s, q in units)
+        sizes = {(s, q): z for z, s, q in units}
+        seq = [sizes[u] for u in got]
+        assert all(a >= b for a, b in zip(seq, seq[1:]))  # longest first
+        for i in range(1, len(got)):  # ties keep sequence order
+            if seq[i] == seq[i - 1]:
+                assert got[i] > got[i - 1]
+    assert L.pa_decode_plan(None, 3, 10, 16, None, 0) == -1
+    assert L.pa_decode_plan(None, 0, 10, 16, None, 0) == 0
+    assert L.pa_decode_plan(None, 0, 10, 0, None, 0) == -1
+
+
+def test_decode_run_argument_errors(L):
+    from paged_kv_cache_326_amd import pa
+
+    c = _cache(pa)
+    d = pa.pa_decode_args()
+    d.cache = ctypes.pointer(c)
+    d.out, d.query, d.block_tables, d.max_blocks_per_seq, d.seq_lens = 0x3000, 0x4000, 0x5000, 4, 0x6000
+    d.num_seqs, d.num_heads, d.max_seq_len, d.scale = 4, 8, 50, 0.125
+    d.workspace, d.workspace_bytes = 0x7000, 1 << 20
+    assert L.pa_decode_run(None, None) == 1
+    d.stage = 3
+    assert L.pa_decode_run(ctypes.byref(d), None) == 2
+    d.stage = 0
+    d.new_key = 0x8000  # fused append needs all three of key, value, slot_mapping
+    assert L.pa_decode_run(ctypes.byref(d), None) == 1
+    d.new_key = 0
+    d.work, d.num_work = 0x9000, 0  # a plan always lists something
+    assert L.pa_decode_run(ctypes.byref(d), None) == 2
+    d.num_work = -1
+    assert L.pa_decode_run(ctypes.byref(d), None) == 2
