@@ -106,12 +106,8 @@ __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
 }
 
 // Two floats -> packed pair in the operand type, round to nearest even.
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
-}
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) { return pack_f16x2(a, b); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return pack_bf16x2(a, b); }
 
 // LDS of one workgroup of NW waves: the partition's block-table slice, and
 // per wave its partial output [G][D], maximum and sum per head for the

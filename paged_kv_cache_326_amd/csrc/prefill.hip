@@ -41,10 +41,16 @@ namespace pa {
 
 namespace {
 
-constexpr int kPW = 4;     // waves per workgroup
-constexpr int kRows = 128; // query rows per workgroup
-constexpr int kKT = 32;    // keys per tile
+constexpr int kPW = 8;          // waves per workgroup
+constexpr int kRows = 32 * kPW; // query rows per workgroup
+constexpr int kKT = 32;         // keys per tile
+constexpr int kRing = 4;        // key tiles in flight in registers
 constexpr int kBtStage = 2048;  // table entries staged in LDS (32K tokens at block size 16)
+// The running maximum of a row is moved only when a tile's maximum exceeds
+// it by more than this (log2 units), so probabilities stay below 2^8 and the
+// accumulator rescale is rare; the final division by the row sum cancels
+// whichever reference maximum was used.
+constexpr float kLazy = 8.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -61,29 +67,16 @@ __device__ __forceinline__ f32x16 mfma32<f16_t>(const u32x4& a, const u32x4& b, 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Two probabilities -> one packed pair of storage elements (round to nearest even).
+// Two floats -> one packed pair of storage elements (round to nearest even).
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi);
 template <>
 __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  return pack_bf16x2(lo, hi);
 }
 template <>
 __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
-  const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
-  const uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
-  return (uint32_t)a | ((uint32_t)b << 16);
-}
-
-template <typename T>
-__device__ __forceinline__ uint16_t to_bits(float x);
-template <>
-__device__ __forceinline__ uint16_t to_bits<bf16_t>(float x) {
-  return f32_to_bf16_bits(x);
-}
-template <>
-__device__ __forceinline__ uint16_t to_bits<f16_t>(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
+  return pack_f16x2(lo, hi);
 }
 
 template <int D>
@@ -101,9 +94,10 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   constexpr int KSTEPS = D / 16;         // QK contraction steps
   constexpr int DT = D / 32;             // O^T row tiles
   constexpr int NT = kPW * 64;
-  constexpr int CPT = kKT * D / 8 / NT;  // 16-byte chunks per thread per tile (K, and V)
+  constexpr int NCHK = kKT * D / 8;      // 16-byte chunks per tile (K, and V)
+  constexpr int CPT = (NCHK + NT - 1) / NT;  // per thread
+  constexpr int RD = kRing;
   using S = PrefillSmem<D>;
-  static_assert(CPT >= 1, "tile too small for the workgroup");
 
   __shared__ __align__(16) uint16_t smem[S::kBytes / 2];
   // Buffer b: K rows at smem + b*(K+V), V^T right after them.
@@ -151,13 +145,25 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   const int limit = row_ok ? ctx + q0 + p : -1;
   const int64_t tok = (int64_t)qbeg + q0 + p;
   const int hq = g * G + h;
+  // The smallest causal limit among this wave's rows that exist: a key tile
+  // that ends at or below it is visible to all of them, unmasked.
+  int lim_min = row_ok ? limit : 0x7fffffff;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, m, 64));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);  // wave-uniform: scalar branches below
 
+  // Q rows as B operands.  A negative scale is moved into Q (negation is
+  // exact), so the logit scale below is never negative and the maximum of
+  // the scaled logits is the scaled maximum.
+  const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[KSTEPS];
   {
     const T* qrow = reinterpret_cast<const T*>(a.query) + (tok * Hq + hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
+      qreg[ks] ^= qflip;
+    }
   }
 
   const T* kc = reinterpret_cast<const T*>(a.cache.key_cache);
@@ -192,11 +198,14 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // divides the block size), copied to LDS as they are.  Keys no row of this
   // workgroup sees (>= kend), or in blocks outside the pool, read as zeros
   // (their probabilities are zero; a zero V keeps 0 * V finite).
-  u32x4 kreg[CPT], vreg[CPT];
-  auto fetch = [&](int t) {
+  // Up to RD tiles are in flight in registers at once: set i holds tile
+  // t with t % RD == i.
+  u32x4 kregs[RD][CPT], vregs[RD][CPT];
+  auto fetch = [&](u32x4 (&kreg)[CPT], u32x4 (&vreg)[CPT], int t) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
+      if (NCHK % NT != 0 && c >= NCHK) continue;
       {
         const int key = c / (D / 8), dch = c % (D / 8);
         const int pos = t * kKT + key;
@@ -229,10 +238,11 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const u32x4 (&kreg)[CPT], const u32x4 (&vreg)[CPT], int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
+      if (NCHK % NT != 0 && c >= NCHK) continue;
       {
         const int key = c / (D / 8), dch = c % (D / 8);
         *reinterpret_cast<u32x4*>(Ks(buf) + key * S::kKStride + dch * 8) = kreg[i];
@@ -250,18 +260,12 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float qscale = a.scale * kLog2e;
+  const float qscale = fabsf(a.scale) * kLog2e;
   // S^T row slot of this lane's A operand, with bits 2 and 3 swapped.
   const int krow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
-
+  // One key tile from LDS buffer buf: scores, online softmax, O^T update.
+  auto tile = [&](int t, int buf) {
     // S^T = K . Q^T
     f32x16 sacc;
 #pragma unroll
@@ -271,40 +275,55 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
     for (int ks = 0; ks < KSTEPS; ++ks)
       sacc = mfma32<T>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], sacc);
 
-    // Online softmax down the column.  Accumulator j holds key
-    // t*32 + 16 (j / 8) + 8 hi + j % 8 (after the row permutation).
-    const int kt0 = t * kKT + 8 * hi;
-    float z[16];
+    // Online softmax down the column, in log2 units.  Accumulator j holds
+    // key t*32 + 16 (j / 8) + 8 hi + j % 8 (after the row permutation).
+    // Tiles that reach past the wave's smallest limit (at most two per
+    // wave: the causal diagonal) mask per key; the rest take every key.
+    const bool masked = t * kKT + kKT - 1 > lim_min;
     float mt = -INFINITY;
+    if (masked) {
+      const int kt0 = t * kKT + 8 * hi;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = kt0 + 16 * (j >> 3) + (j & 7);
-      z[j] = key <= limit ? sacc[j] * qscale : -INFINITY;
-      mt = fmaxf(mt, z[j]);
+      for (int j = 0; j < 16; ++j) {
+        const int key = kt0 + 16 * (j >> 3) + (j & 7);
+        sacc[j] = key <= limit ? sacc[j] * qscale : -INFINITY;
+        mt = fmaxf(mt, sacc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[j]);
+      mt *= qscale;
     }
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f;
-    float pj[16];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = 0.f;
-    } else {
-      alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = z[j] == -INFINITY ? 0.f : fast_exp2(z[j] - m_new);
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ps += pj[j];
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
+    // Move the reference maximum (and rescale) only where the tile exceeds
+    // it by more than kLazy; the whole wave skips the rescale when no row
+    // needs it.
+    const bool move = mt > m_run + kLazy;
+    if (__any(move)) {
+      const float m_new = move ? mt : m_run;
+      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
     }
+    // A row that has seen no key yet (m_run = -inf) only holds masked
+    // logits: exp2(-inf) = 0 with any finite reference.
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    float pj[16];
+    if (masked) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(sacc[j] - m_ref);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(fmaf(sacc[j], qscale, -m_ref));
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ps += pj[j];
+    l_run += ps;
     // P^T as B operands.  f16 keeps 11 significant bits, enough on its own;
     // bf16 keeps 8, so P is split into a bf16 head and a bf16 remainder and
     // both are multiplied (the V^T operand is read once for the two).
@@ -315,11 +334,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       for (int i = 0; i < 4; ++i) {
         const float x0 = pj[8 * ks + 2 * i], x1 = pj[8 * ks + 2 * i + 1];
         pb[ks][i] = pack2<T>(x0, x1);
-        if constexpr (Elem<T>::kBytes == 2 && !std::is_same<T, f16_t>::value) {
-          const float h0 = __uint_as_float((pb[ks][i] & 0xffffu) << 16);
-          const float h1 = __uint_as_float(pb[ks][i] & 0xffff0000u);
-          pl[ks][i] = pack2<T>(x0 - h0, x1 - h1);
-        }
+        if constexpr (std::is_same<T, bf16_t>::value)
+          pl[ks][i] = pack2<T>(x0 - bf16_lo(pb[ks][i]), x1 - bf16_hi(pb[ks][i]));
       }
 
     // O^T += V^T . P^T
@@ -330,12 +346,34 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 va = *reinterpret_cast<const u32x4*>(vrp + 16 * ks);
         o[dt] = mfma32<T>(va, pb[ks], o[dt]);
-        if constexpr (!std::is_same<T, f16_t>::value) o[dt] = mfma32<T>(va, pl[ks], o[dt]);
+        if constexpr (std::is_same<T, bf16_t>::value) o[dt] = mfma32<T>(va, pl[ks], o[dt]);
       }
     }
+  };
 
-    if (t + 1 < ntiles) stash(buf ^ 1);
-    __syncthreads();
+  // Pipeline: tile t is used from LDS buffer t & 1 while tile t+1 waits in
+  // registers for its LDS copy and tiles t+2 .. t+RD are loading.  After
+  // tile t, set (t+1) % RD goes to LDS and is refilled with tile t+1+RD.
+#pragma unroll
+  for (int i = 0; i < RD; ++i)
+    if (i < ntiles) fetch(kregs[i], vregs[i], i);
+  stash(kregs[0], vregs[0], 0);
+  if (RD < ntiles) fetch(kregs[0], vregs[0], RD);
+  __syncthreads();
+
+  for (int t0 = 0; t0 < ntiles; t0 += RD) {
+#pragma unroll
+    for (int i = 0; i < RD; ++i) {
+      const int t = t0 + i;
+      if (t < ntiles) {
+        tile(t, t & 1);
+        if (t + 1 < ntiles) {
+          stash(kregs[(i + 1) % RD], vregs[(i + 1) % RD], (t + 1) & 1);
+          if (t + 1 + RD < ntiles) fetch(kregs[(i + 1) % RD], vregs[(i + 1) % RD], t + 1 + RD);
+        }
+        __syncthreads();
+      }
+    }
   }
 
   // Normalise and store this lane's row: accumulator j of tile dt is
@@ -350,8 +388,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       for (int j4 = 0; j4 < 4; ++j4) {
         const int d = 32 * dt + 8 * j4 + 4 * hi;
         u32x2 pk;
-        pk[0] = (uint32_t)to_bits<T>(o[dt][4 * j4] * inv) | ((uint32_t)to_bits<T>(o[dt][4 * j4 + 1] * inv) << 16);
-        pk[1] = (uint32_t)to_bits<T>(o[dt][4 * j4 + 2] * inv) | ((uint32_t)to_bits<T>(o[dt][4 * j4 + 3] * inv) << 16);
+        pk[0] = pack2<T>(o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv);
+        pk[1] = pack2<T>(o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + d) = pk;
       }
   }
