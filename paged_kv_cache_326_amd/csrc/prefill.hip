@@ -10,16 +10,20 @@
 // (ctx = seq_len - q_s; the chunk's own K/V are already in the pool) and
 // attends causally: position ctx+i sees keys 0 .. ctx+i.
 //
-// Work decomposition.  A workgroup (4 waves) owns 128 query rows that share
-// one KV head: the G heads of the group times 128/G consecutive positions.
+// Work decomposition.  A workgroup (8 waves) owns 256 query rows that share
+// one KV head: the G heads of the group times 256/G consecutive positions.
 // Each wave owns 32 rows.  Keys stream through in tiles of 32: the tile's K
-// rows ([32][D]) and V^T ([D][32], as the pool stores value tiles) are staged in LDS
-// (double-buffered: the next tile's global loads are in flight while the
-// current tile is used), then per wave
+// rows ([32][D]) and V^T ([D][32], as the pool stores value tiles) are staged
+// in LDS, then per wave
 //   S^T[32 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16 over D
 //   online softmax down each column (a column is one query row, held by a
 //   lane pair), P^T rounded to the storage type in registers
 //   O^T[D x 32 rows]     += V^T . P^T    v_mfma_f32_32x32x16 over the tile
+// The loop is software-pipelined so that matrix and vector work of one wave
+// overlap: while tile t's softmax runs on the vector ALU, the scores of tile
+// t+1 are computed on the matrix cores.  LDS holds three tile stages (t,
+// t+1 and t+2, written while t is used), and a ring of register sets keeps
+// the global loads of later tiles in flight.
 // Computing the transposed products keeps every operand a 16-byte LDS or
 // register read: the accumulator layout of S^T is directly the B operand of
 // the PV product once the S^T rows (keys) are permuted by swapping index bits
@@ -44,7 +48,7 @@ namespace {
 constexpr int kPW = 8;          // waves per workgroup
 constexpr int kRows = 32 * kPW; // query rows per workgroup
 constexpr int kKT = 32;         // keys per tile
-constexpr int kRing = 4;        // key tiles in flight in registers
+constexpr int kRing = 3;        // key tiles in flight in registers
 constexpr int kBtStage = 2048;  // table entries staged in LDS (32K tokens at block size 16)
 // The running maximum of a row is moved only when a tile's maximum exceeds
 // it by more than this (log2 units), so probabilities stay below 2^8 and the
@@ -85,8 +89,19 @@ struct PrefillSmem {
   static constexpr int kVStride = kKT + 8;   // V^T row stride (elements)
   static constexpr int kKElems = kKT * kKStride;
   static constexpr int kVElems = D * kVStride;
-  static constexpr int kBytes = 2 * (kKElems + kVElems) * 2;
+  static constexpr int kStage = kKElems + kVElems;  // one tile: K rows, then V^T
+  static constexpr int kStages = 3;
+  static constexpr int kBytes = kStages * kStage * 2;
 };
+
+// max(x, x of the lane 32 away): one v_permlane32_swap exchanges the upper
+// half of the first operand with the lower half of the second, so with both
+// operands x each lane holds its own value in one result and its partner's
+// in the other.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <typename T, int D, int B, int G>
 __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2))) prefill_kernel(PrefillArgs a) {
@@ -97,12 +112,12 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   constexpr int NCHK = kKT * D / 8;      // 16-byte chunks per tile (K, and V)
   constexpr int CPT = (NCHK + NT - 1) / NT;  // per thread
   constexpr int RD = kRing;
+  static_assert(RD >= 2, "the prologue stages two tiles from the ring");
   using S = PrefillSmem<D>;
 
   __shared__ __align__(16) uint16_t smem[S::kBytes / 2];
-  // Buffer b: K rows at smem + b*(K+V), V^T right after them.
-  auto Ks = [&](int b) { return smem + b * (S::kKElems + S::kVElems); };
-  auto Vt = [&](int b) { return smem + b * (S::kKElems + S::kVElems) + S::kKElems; };
+  auto Ks = [&](int st) { return smem + st * S::kStage; };
+  auto Vt = [&](int st) { return smem + st * S::kStage + S::kKElems; };
 
   // Work item.  Workgroup ids are dealt to the 8 XCDs round-robin; remap so
   // that consecutive work items (the query tiles of one sequence and KV head,
@@ -198,8 +213,7 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // divides the block size), copied to LDS as they are.  Keys no row of this
   // workgroup sees (>= kend), or in blocks outside the pool, read as zeros
   // (their probabilities are zero; a zero V keeps 0 * V finite).
-  // Up to RD tiles are in flight in registers at once: set i holds tile
-  // t with t % RD == i.
+  // Up to RD tiles are in flight in registers at once.
   u32x4 kregs[RD][CPT], vregs[RD][CPT];
   auto fetch = [&](u32x4 (&kreg)[CPT], u32x4 (&vreg)[CPT], int t) {
 #pragma unroll
@@ -238,18 +252,18 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       }
     }
   };
-  auto stash = [&](const u32x4 (&kreg)[CPT], const u32x4 (&vreg)[CPT], int buf) {
+  auto stash = [&](const u32x4 (&kreg)[CPT], const u32x4 (&vreg)[CPT], int st) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (NCHK % NT != 0 && c >= NCHK) continue;
       {
         const int key = c / (D / 8), dch = c % (D / 8);
-        *reinterpret_cast<u32x4*>(Ks(buf) + key * S::kKStride + dch * 8) = kreg[i];
+        *reinterpret_cast<u32x4*>(Ks(st) + key * S::kKStride + dch * 8) = kreg[i];
       }
       {
         const int kg = c % (kKT / 8), d = c / (kKT / 8);
-        *reinterpret_cast<u32x4*>(Vt(buf) + d * S::kVStride + kg * 8) = vreg[i];
+        *reinterpret_cast<u32x4*>(Vt(st) + d * S::kVStride + kg * 8) = vreg[i];
       }
     }
   };
@@ -264,70 +278,64 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // S^T row slot of this lane's A operand, with bits 2 and 3 swapped.
   const int krow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  // One key tile from LDS buffer buf: scores, online softmax, O^T update.
-  auto tile = [&](int t, int buf) {
-    // S^T = K . Q^T
-    f32x16 sacc;
+  // S^T = K . Q^T for the tile in stage st.
+  auto scores = [&](int st) {
+    f32x16 acc;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-    const uint16_t* krp = Ks(buf) + krow * S::kKStride + 8 * hi;
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+    const uint16_t* krp = Ks(st) + krow * S::kKStride + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      sacc = mfma32<T>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], sacc);
+      acc = mfma32<T>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], acc);
+    return acc;
+  };
 
-    // Online softmax down the column, in log2 units.  Accumulator j holds
-    // key t*32 + 16 (j / 8) + 8 hi + j % 8 (after the row permutation).
-    // Tiles that reach past the wave's smallest limit (at most two per
-    // wave: the causal diagonal) mask per key; the rest take every key.
-    const bool masked = t * kKT + kKT - 1 > lim_min;
+  // Online softmax of tile t's scores down the column, in log2 units, into
+  // the P^T operands.  Accumulator j holds key t*32 + 16 (j / 8) + 8 hi +
+  // j % 8 (after the row permutation).  Only tiles that reach past the
+  // wave's smallest limit (the causal diagonal) mask per key.  The running
+  // maximum moves only where the tile exceeds it by more than kLazy; the
+  // probabilities are taken against the moved maximum and the accumulator
+  // rescale (rare) is left to the caller through alpha.
+  u32x4 pb[2], pl[2];
+  auto softmax = [&](f32x16 sc, int t, bool masked, float& alpha) {
     float mt = -INFINITY;
     if (masked) {
       const int kt0 = t * kKT + 8 * hi;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = kt0 + 16 * (j >> 3) + (j & 7);
-        sacc[j] = key <= limit ? sacc[j] * qscale : -INFINITY;
-        mt = fmaxf(mt, sacc[j]);
+        sc[j] = key <= limit ? sc[j] * qscale : -INFINITY;
+        mt = fmaxf(mt, sc[j]);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[j]);
+      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sc[j]);
       mt *= qscale;
     }
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    // Move the reference maximum (and rescale) only where the tile exceeds
-    // it by more than kLazy; the whole wave skips the rescale when no row
-    // needs it.
+    mt = max_across_halves(mt);
     const bool move = mt > m_run + kLazy;
-    if (__any(move)) {
-      const float m_new = move ? mt : m_run;
-      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
+    const float m_new = move ? mt : m_run;
+    alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
+    m_run = m_new;
     // A row that has seen no key yet (m_run = -inf) only holds masked
     // logits: exp2(-inf) = 0 with any finite reference.
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float pj[16];
     if (masked) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(sacc[j] - m_ref);
+      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(sc[j] - m_ref);
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(fmaf(sacc[j], qscale, -m_ref));
+      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(fmaf(sc[j], qscale, -m_ref));
     }
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) ps += pj[j];
-    l_run += ps;
+    l_run = l_run * alpha + ps;
     // P^T as B operands.  f16 keeps 11 significant bits, enough on its own;
     // bf16 keeps 8, so P is split into a bf16 head and a bf16 remainder and
     // both are multiplied (the V^T operand is read once for the two).
-    u32x4 pb[2], pl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -337,11 +345,13 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
         if constexpr (std::is_same<T, bf16_t>::value)
           pl[ks][i] = pack2<T>(x0 - bf16_lo(pb[ks][i]), x1 - bf16_hi(pb[ks][i]));
       }
+  };
 
-    // O^T += V^T . P^T
+  // O^T += V^T . P^T for the tile in stage st.
+  auto accumulate = [&](int st) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vrp = Vt(buf) + (32 * dt + n) * S::kVStride + 8 * hi;
+      const uint16_t* vrp = Vt(st) + (32 * dt + n) * S::kVStride + 8 * hi;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 va = *reinterpret_cast<const u32x4*>(vrp + 16 * ks);
@@ -351,27 +361,54 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
-  // Pipeline: tile t is used from LDS buffer t & 1 while tile t+1 waits in
-  // registers for its LDS copy and tiles t+2 .. t+RD are loading.  After
-  // tile t, set (t+1) % RD goes to LDS and is refilled with tile t+1+RD.
+  // Prologue: tiles 0 .. RD-1 load into the register sets, tiles 0 and 1 go
+  // to stages 0 and 1 and their sets are refilled with tiles RD and RD+1.
 #pragma unroll
   for (int i = 0; i < RD; ++i)
     if (i < ntiles) fetch(kregs[i], vregs[i], i);
   stash(kregs[0], vregs[0], 0);
+  if (1 < ntiles) stash(kregs[1], vregs[1], 1);
   if (RD < ntiles) fetch(kregs[0], vregs[0], RD);
+  if (RD + 1 < ntiles) fetch(kregs[1], vregs[1], RD + 1);
   __syncthreads();
+  f32x16 sc = scores(0);
 
+  // Iteration t: scores of tile t+1 (stage (t+1) % 3; past the last tile
+  // the stage holds stale data and the result goes unused) with tile t's
+  // softmax, then tile t's PV product (stage t % 3), then tile t+2 from its
+  // register set into stage (t+2) % 3, whose last reader was tile t-1, and
+  // the set refilled with tile t+2+RD.
   for (int t0 = 0; t0 < ntiles; t0 += RD) {
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
       const int t = t0 + i;
       if (t < ntiles) {
-        tile(t, t & 1);
-        if (t + 1 < ntiles) {
-          stash(kregs[(i + 1) % RD], vregs[(i + 1) % RD], (t + 1) & 1);
-          if (t + 1 + RD < ntiles) fetch(kregs[(i + 1) % RD], vregs[(i + 1) % RD], t + 1 + RD);
+        // Stage of tile t (a constant when RD is a multiple of 3).
+        const int st0 = RD % 3 == 0 ? i % 3 : t % 3;
+        const int st1 = st0 == 2 ? 0 : st0 + 1;
+        const int st2 = st1 == 2 ? 0 : st1 + 1;
+        float alpha;
+        f32x16 sn;
+        if (t * kKT + kKT - 1 > lim_min) {
+          sn = scores(st1);
+          softmax(sc, t, true, alpha);
+        } else {
+          sn = scores(st1);
+          softmax(sc, t, false, alpha);
+        }
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+        }
+        accumulate(st0);
+        if (t + 2 < ntiles) {
+          stash(kregs[(i + 2) % RD], vregs[(i + 2) % RD], st2);
+          if (t + 2 + RD < ntiles) fetch(kregs[(i + 2) % RD], vregs[(i + 2) % RD], t + 2 + RD);
         }
         __syncthreads();
+        sc = sn;
       }
     }
   }
