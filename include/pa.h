@@ -425,6 +425,52 @@ int32_t pa_bm_drop_version(pa_block_manager* bm, uint64_t version);
 int32_t pa_bm_cached_blocks(pa_block_manager* bm);
 int32_t pa_bm_is_cached(pa_block_manager* bm, int32_t block);
 pa_status pa_bm_set_hash_bits(pa_block_manager* bm, int32_t bits);
+int32_t pa_bm_block_size(pa_block_manager* bm);
+
+/* Continuous-batching step arithmetic (host only, thread-safe per scheduler).
+ * [P1] "生产级推理引擎的内存管理与调度": one scheduling call per iteration
+ * decides which requests take part, in three steps:
+ *   1. every decoding request whose prompt + generated tokens need more
+ *      blocks than it owns (ceil(tokens / block_size) > owned) takes one
+ *      more block from the pool and is scheduled; if the pool is empty the
+ *      request is preempted for this iteration (not scheduled, keeps its
+ *      blocks); a request needing no block is scheduled;
+ *   2. while fewer than max_batch_size requests are scheduled, the front of
+ *      the FIFO waiting queue is admitted (its ceil(prompt / block_size)
+ *      blocks allocated, state decoding) if the pool holds them, else it
+ *      stays at the front and admission stops for this iteration;
+ *   3. requests that have generated max_tokens tokens release their blocks.
+ * Active requests are visited in admission order.  The scheduler keeps its
+ * requests' blocks in the block manager it is given (sequence id = request
+ * id; their tables are read with pa_bm_block_table); it does not own the
+ * manager, which must outlive it.
+ *
+ * pa_sched_create       NULL on bad arguments (max_batch_size < 1)
+ * pa_sched_add_request  queue a request; max_tokens >= 1 and prompt_len >= 0
+ *                       (PA_ERR_SHAPE), id unused in the scheduler and the
+ *                       manager (PA_ERR_EXISTS)
+ * pa_sched_schedule     run one iteration's three steps; writes up to
+ *                       capacity scheduled ids (decoding requests in
+ *                       admission order, then the newly admitted) and their
+ *                       count to *num_scheduled
+ * pa_sched_step         one token generated by a decoding request
+ *                       (PA_ERR_NOT_FOUND for any other id); reaching
+ *                       max_tokens finishes it (released by the next
+ *                       pa_sched_schedule)
+ * pa_sched_state        0 waiting, 1 decoding, 2 finished, -1 unknown or
+ *                       released
+ * pa_sched_generated    tokens generated so far, -1 unknown or released
+ */
+typedef struct pa_scheduler pa_scheduler;
+pa_scheduler* pa_sched_create(pa_block_manager* bm, int32_t max_batch_size);
+void pa_sched_destroy(pa_scheduler* sched);
+pa_status pa_sched_add_request(pa_scheduler* sched, int64_t request_id, int32_t prompt_len, int32_t max_tokens);
+pa_status pa_sched_schedule(pa_scheduler* sched, int64_t* scheduled, int32_t capacity, int32_t* num_scheduled);
+pa_status pa_sched_step(pa_scheduler* sched, int64_t request_id);
+int32_t pa_sched_state(pa_scheduler* sched, int64_t request_id);
+int32_t pa_sched_generated(pa_scheduler* sched, int64_t request_id);
+int32_t pa_sched_num_waiting(pa_scheduler* sched);
+int32_t pa_sched_num_active(pa_scheduler* sched);
 
 const char* pa_status_string(pa_status status);
 const char* pa_version(void);

@@ -27,6 +27,9 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   prefill_attention    torch SDPA causal / explicit-mask special cases
   BlockPoolModel       FIFO order and conservation of blocks, reference
                        counts under sharing, brute-force block counts
+  SchedulerModel       hand-worked iterations of the three scheduling steps
+                       (admission, head-of-line wait, preemption, release),
+                       conservation, batch limit and block-need invariants
   fp8 (E4M3 codes)     torch float8_e4m3fn values and rounding, hand-worked
                        values, exact midpoints, brute-force nearest,
                        saturation and quantisation error bounds
@@ -43,6 +46,7 @@ from .paging import (  # noqa: F401
 )
 from .attention import decode_attention, prefill_attention  # noqa: F401
 from .block_pool import BlockPoolModel, NoBlocks, copy_blocks, gather_blocks, scatter_blocks  # noqa: F401
+from .scheduler import SchedulerModel  # noqa: F401
 from .fp8 import (  # noqa: F401
     FP8_MAX,
     E4M3_VALUES,

@@ -210,6 +210,8 @@ pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, const int
 
 void pa_bm_destroy(pa_block_manager* m) { delete m; }
 
+int32_t pa_bm_block_size(pa_block_manager* m) { return m ? m->block_size : -1; }
+
 int32_t pa_bm_available(pa_block_manager* m) {
   if (!m) return -1;
   std::lock_guard<std::mutex> g(m->mu);

@@ -25,7 +25,10 @@ if hasattr(torch, "float8_e4m3fn"):
     _DTYPE[torch.float8_e4m3fn] = PA_FP8_E4M3
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH",
            6: "PA_ERR_NO_BLOCKS", 7: "PA_ERR_NOT_FOUND", 8: "PA_ERR_EXISTS"}
+PA_ERR_SHAPE = 2
 PA_ERR_NO_BLOCKS = 6
+PA_ERR_NOT_FOUND = 7
+PA_ERR_EXISTS = 8
 
 
 class PaError(RuntimeError):
@@ -111,6 +114,16 @@ EXPORTS = (
     "pa_bm_cached_blocks",
     "pa_bm_is_cached",
     "pa_bm_set_hash_bits",
+    "pa_bm_block_size",
+    "pa_sched_create",
+    "pa_sched_destroy",
+    "pa_sched_add_request",
+    "pa_sched_schedule",
+    "pa_sched_step",
+    "pa_sched_state",
+    "pa_sched_generated",
+    "pa_sched_num_waiting",
+    "pa_sched_num_active",
     "pa_status_string",
     "pa_version",
 )
@@ -200,6 +213,25 @@ def lib() -> ctypes.CDLL:
     L.pa_bm_is_cached.restype = i32
     L.pa_bm_set_hash_bits.argtypes = [bm, i32]
     L.pa_bm_set_hash_bits.restype = ctypes.c_int
+    L.pa_bm_block_size.argtypes = [bm]
+    L.pa_bm_block_size.restype = i32
+    sc = ctypes.c_void_p
+    L.pa_sched_create.argtypes = [bm, i32]
+    L.pa_sched_create.restype = sc
+    L.pa_sched_destroy.argtypes = [sc]
+    L.pa_sched_destroy.restype = None
+    L.pa_sched_add_request.argtypes = [sc, i64, i32, i32]
+    L.pa_sched_add_request.restype = ctypes.c_int
+    L.pa_sched_schedule.argtypes = [sc, vp, i32, vp]
+    L.pa_sched_schedule.restype = ctypes.c_int
+    L.pa_sched_step.argtypes = [sc, i64]
+    L.pa_sched_step.restype = ctypes.c_int
+    for name in ("pa_sched_state", "pa_sched_generated"):
+        getattr(L, name).argtypes = [sc, i64]
+        getattr(L, name).restype = i32
+    for name in ("pa_sched_num_waiting", "pa_sched_num_active"):
+        getattr(L, name).argtypes = [sc]
+        getattr(L, name).restype = i32
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -635,6 +667,55 @@ class BlockManager:
 
     def set_hash_bits(self, bits: int):
         _check(lib().pa_bm_set_hash_bits(self._h, int(bits)), "pa_bm_set_hash_bits")
+
+
+class Scheduler:
+    """The library's continuous-batching step arithmetic over a BlockManager
+    (request ids are the manager's sequence ids)."""
+
+    WAITING, DECODING, FINISHED = 0, 1, 2
+
+    def __init__(self, manager: BlockManager, max_batch_size: int):
+        self._bm = manager  # keeps the manager alive while the scheduler uses it
+        self._h = lib().pa_sched_create(manager._h, int(max_batch_size))
+        if not self._h:
+            raise ValueError("pa_sched_create rejected its arguments")
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        self._h = None
+        if h and _lib is not None:
+            _lib.pa_sched_destroy(h)
+
+    __del__ = close
+
+    def add_request(self, request_id: int, prompt_len: int, max_tokens: int):
+        _check(lib().pa_sched_add_request(self._h, int(request_id), int(prompt_len), int(max_tokens)),
+               "pa_sched_add_request")
+
+    def schedule(self):
+        """One iteration; returns the scheduled request ids in order."""
+        L = lib()
+        n = ctypes.c_int32()
+        cap = max(L.pa_sched_num_active(self._h) + L.pa_sched_num_waiting(self._h), 1)
+        buf = (ctypes.c_int64 * cap)()
+        _check(L.pa_sched_schedule(self._h, buf, cap, ctypes.addressof(n)), "pa_sched_schedule")
+        return list(buf[: n.value])
+
+    def step(self, request_id: int):
+        _check(lib().pa_sched_step(self._h, int(request_id)), "pa_sched_step")
+
+    def state(self, request_id: int) -> int:
+        return int(lib().pa_sched_state(self._h, int(request_id)))
+
+    def generated(self, request_id: int) -> int:
+        return int(lib().pa_sched_generated(self._h, int(request_id)))
+
+    def num_waiting(self) -> int:
+        return int(lib().pa_sched_num_waiting(self._h))
+
+    def num_active(self) -> int:
+        return int(lib().pa_sched_num_active(self._h))
 
 
 def version() -> str:
