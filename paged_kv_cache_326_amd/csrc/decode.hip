@@ -35,8 +35,8 @@
 //   16x16x32 f16/bf16: A[m][k] m = r, k = 8g + e (e < 8); B[k][n] k = 8g + e, n = r
 //   16x16x4 f32:       A[m][k] m = r, k = g;             B[k][n] k = g, n = r
 //   C[m][n]: m = 4g + j, n = r
-// FP8 codes are widened exactly to f16 (value * 2^-8) on the way into the
-// f16 products; bf16 probabilities enter the PV product as a bf16 hi + lo
+// FP8 codes are converted exactly to f16 (v_cvt_scalef32_pk_f16_fp8, two
+// codes per instruction) on the way into the f16 products; bf16 probabilities enter the PV product as a bf16 hi + lo
 // pair (two products), f16 ones rounded to f16 with the normaliser summing
 // the same rounded values.
 //
@@ -99,10 +99,13 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Four E4M3 codes (one word) -> two f16x2 words (values * 2^-8).
+// Four E4M3 codes (one word) -> two f16x2 words holding their values
+// (bytes 0, 1 in lo, 2, 3 in hi, low byte in the low half).  Every E4M3 value
+// (magnitudes 2^-9 .. 448) is an f16 normal number, so the conversion at
+// scale 1 is exact.
 __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes01));
-  hi = e4m3_pair_to_f16x2(__builtin_amdgcn_perm(w, w, kPermBytes23));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 // Two floats -> packed pair in the operand type, round to nearest even.
@@ -310,8 +313,9 @@ decode_partition_kernel(DecodeArgs a) {
   const int64_t blk_stride = (int64_t)Hkv * B * D;
   const T* kbase = reinterpret_cast<const T*>(a.cache.key_cache) + (int64_t)g * B * D;
   const T* vbase = reinterpret_cast<const T*>(a.cache.value_cache) + (int64_t)g * D * B;
-  // FP8: widened K values are the codes' values * 2^-8.
-  const float qscale = kFp8 ? a.scale * kLog2e * 256.f * a.cache.k_scale : a.scale * kLog2e;
+  // FP8: the widened K values are the codes' values; the pool scale joins
+  // the logit scale.
+  const float qscale = kFp8 ? a.scale * kLog2e * a.cache.k_scale : a.scale * kLog2e;
 
   struct Buf {
     u32x4 k[2][NLK];        // K rows of the two 16-token halves
@@ -519,8 +523,8 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // FP8: widened V values are the codes' values * 2^-8.
-  const float vfac = kFp8 ? 256.f * a.cache.v_scale : 1.f;
+  // FP8: the widened V values are the codes' values.
+  const float vfac = kFp8 ? a.cache.v_scale : 1.f;
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D;
     const int d = idx % D;

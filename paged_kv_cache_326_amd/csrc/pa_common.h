@@ -99,21 +99,6 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (r - (120u << 3));
 }
 
-// Two E4M3 codes held in bits 15:8 and 31:24 of x (other bits zero) -> an
-// f16x2 word whose halves equal the codes' values times 2^-8, exactly: the
-// sign stays in bit 15 and the 7 exponent+mantissa bits move down one place,
-// so the E4M3 exponent field (bias 7) becomes the low four bits of the f16
-// exponent field (bias 15) and subnormals stay subnormal.  Code 0x7f (NaN)
-// maps to a finite value; quantised pools never hold it.
-__device__ __forceinline__ uint32_t e4m3_pair_to_f16x2(uint32_t x) {
-  return (x & 0x80008000u) | ((x >> 1) & 0x3f803f80u);
-}
-
-// v_perm_b32 selectors that place two bytes of a word in bits 15:8 and
-// 31:24 (zeros elsewhere): bytes (0, 1) and (2, 3) of the second operand.
-constexpr uint32_t kPermBytes01 = 0x010c000cu;
-constexpr uint32_t kPermBytes23 = 0x030c020cu;
-
 // Unpack one 32-bit word holding two storage elements (or one f32) to floats.
 template <typename T>
 __device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b);
