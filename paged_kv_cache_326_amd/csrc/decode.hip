@@ -141,6 +141,9 @@ __host__ __device__ inline SmemLayout smem_layout(int partition, int B, int G, i
 // all issued before any is used; batches combine with a running rescale.
 constexpr int kMergeBatch = 16;
 
+// Lazy rescale threshold of the online softmax (log2 units).
+constexpr float kLazy = 8.f;
+
 // np partitions of the sequence are merged; rows are num_partitions apart.
 template <int D>
 __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
@@ -406,14 +409,21 @@ decode_partition_kernel(DecodeArgs a) {
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+    // The reference maximum moves only when the step exceeds it by more
+    // than kLazy (log2 units), so probabilities stay below 2^kLazy and the
+    // accumulator rescale is rare; the final division by the sum cancels
+    // whichever reference was used.
+    const bool move = mx > m_run + kLazy;
+    const float m_new = move ? mx : m_run;
+    const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = z[e] == -INFINITY ? 0.f : fast_exp2(z[e] - m_new);
     m_run = m_new;
+    if (__any(move)) {
 #pragma unroll
-    for (int dd = 0; dd < NDT; ++dd) o[dd] *= alpha;
+      for (int dd = 0; dd < NDT; ++dd) o[dd] *= alpha;
+    }
 
     // Value tokens past the end (or in a block outside the pool) are zeroed:
     // their probabilities are 0 and 0 * NaN would poison the sums.

@@ -201,3 +201,28 @@ def fp8_pool_oracle(w: synth.Workload, scales):
     import oracle
 
     return oracle.fp8_quantize(w.key_cache, scales[0]), oracle.fp8_quantize(w.value_cache, scales[1])
+
+
+def ramped_keys(w, slope, seed):
+    """Keys whose logits grow by `slope` per position along every sequence
+    (key j = (c + slope j) u + small noise, queries = u), written both into
+    the cached part of the pool and into the chunk's new rows."""
+    import dataclasses
+
+    rng = np.random.default_rng(seed)
+    D, B = w.head_dim, w.block_size
+    u = np.ones(D) / np.sqrt(D)
+    kc = np.array(w.key_cache, copy=True)
+    nk = np.array(w.new_key, copy=True)
+    cu = w.cu_q_lens
+    for s in range(w.num_seqs):
+        L, q = int(w.seq_lens[s]), int(w.q_lens[s])
+        for j in range(L):
+            row = (0.5 + slope * j) * u + 0.01 * rng.standard_normal((w.num_kv_heads, D))
+            row = synth.f32_to_storage(row.astype(np.float32), w.dtype)
+            if j < L - q:
+                kc[w.block_tables[s, j // B], :, j % B, :] = row
+            else:
+                nk[cu[s] + j - (L - q)] = row
+    qry = synth.f32_to_storage(np.broadcast_to(u, w.query.shape).astype(np.float32), w.dtype)
+    return dataclasses.replace(w, key_cache=kc, new_key=nk, query=np.ascontiguousarray(qry))

@@ -363,3 +363,21 @@ def test_decode_shared_prefix_bit_identical_to_private_copies():
     b = harness.GpuWorkload(priv).step()
     _sync()
     assert np.array_equal(harness.from_device(a, w.dtype).view(np.uint8), harness.from_device(b, w.dtype).view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("slope", [0.02, 0.15, 1.5])
+@pytest.mark.parametrize("partition", [0, 512])
+def test_decode_growing_logits(dt, slope, partition):
+    # Logits rise along the tokens: per 32-token step by less than the lazy
+    # rescale threshold (the reference maximum stays, probabilities grow
+    # towards 2^8), by about it, and by far more (a rescale every step);
+    # with 512-token partitions the split partials carry stale references.
+    w = synth.custom(seed=21, dtype=dt, num_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                     seq_lens=[40, 700, 3000])
+    w = harness.ramped_keys(w, slope / w.scale, seed=5)
+    gw = harness.GpuWorkload(w)
+    out = gw.step(partition_size=partition)
+    _sync()
+    _, _, _, ref = harness.oracle_step(w)
+    _assert_close(_as64(out, w.dtype), ref, w.dtype, f"decode {dt} ramp {slope} P={partition}")

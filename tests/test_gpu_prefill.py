@@ -137,31 +137,6 @@ def test_prefill_scale_sign_and_zero(scale):
     _check(out, harness.oracle_prefill(w, kc, vc), w.dtype, f"prefill scale {scale}")
 
 
-def _ramped(w, slope, seed):
-    """Keys whose logits grow by `slope` per position along every sequence
-    (key j = (c + slope j) u + small noise, queries = u), written both into
-    the cached part of the pool and into the chunk's new rows."""
-    import dataclasses
-
-    rng = np.random.default_rng(seed)
-    D, B = w.head_dim, w.block_size
-    u = np.ones(D) / np.sqrt(D)
-    kc = np.array(w.key_cache, copy=True)
-    nk = np.array(w.new_key, copy=True)
-    cu = w.cu_q_lens
-    for s in range(w.num_seqs):
-        L, q = int(w.seq_lens[s]), int(w.q_lens[s])
-        for j in range(L):
-            row = (0.5 + slope * j) * u + 0.01 * rng.standard_normal((w.num_kv_heads, D))
-            row = synth.f32_to_storage(row.astype(np.float32), w.dtype)
-            if j < L - q:
-                kc[w.block_tables[s, j // B], :, j % B, :] = row
-            else:
-                nk[cu[s] + j - (L - q)] = row
-    qry = synth.f32_to_storage(np.broadcast_to(u, w.query.shape).astype(np.float32), w.dtype)
-    return dataclasses.replace(w, key_cache=kc, new_key=nk, query=np.ascontiguousarray(qry))
-
-
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("slope", [0.02, 0.15, 1.5])
 def test_prefill_growing_logits(dt, slope):
@@ -170,7 +145,7 @@ def test_prefill_growing_logits(dt, slope):
     # towards 2^8), by about it, and by far more (a rescale every tile).
     w = synth.custom(seed=11, dtype=dt, num_heads=8, num_kv_heads=1, head_dim=64, block_size=16,
                      seq_lens=[700, 160], q_lens=[100, 160], pool_factor=1.0)
-    w = _ramped(w, slope / w.scale, seed=3)
+    w = harness.ramped_keys(w, slope / w.scale, seed=3)
     gw = harness.GpuWorkload(w)
     gw.slots()
     gw.scatter()
