@@ -40,7 +40,7 @@
  *
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype f32, f16, bf16
- * (prefill: f16, bf16).
+ * (prefill: f16, bf16, FP8).
  *
  * Thread safety: no global mutable state; calls on different streams may run
  * concurrently as long as their output buffers do not overlap.
@@ -310,13 +310,16 @@ int32_t pa_decode_plan(const int32_t* seq_lens_host, int32_t num_seqs, int32_t m
  *     out[t][h] = softmax_j(scale * q[t][h] . K[s][j]) . V[s][j],  j <= ctx+i.
  *
  * out, query   [cu_q_lens[num_seqs]][num_heads][head_dim], cache->dtype
- *              (f16 or bf16; rounded to nearest-even; other pool dtypes
- *              return PA_ERR_UNSUPPORTED)
+ *              for f16 and bf16 pools, float16 for an FP8 pool (whose codes
+ *              are converted exactly to f16 on chip and whose scales apply
+ *              as in pa_decode); rounded to nearest-even; float32 pools
+ *              return PA_ERR_UNSUPPORTED
  * cu_q_lens    int32 [num_seqs + 1]
  * seq_lens     int32 [num_seqs], >= the sequence's chunk length
  * max_q_len    host-side upper bound of the chunk lengths
  * Products run on v_mfma_f32_32x32x16 with fp32 accumulation; the softmax
- * probabilities enter the PV product rounded to the cache dtype.
+ * probabilities enter the PV product rounded to the operand dtype (f16 for
+ * an FP8 pool; bf16 as a head and remainder pair).
  */
 pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* query,
                            const int32_t* cu_q_lens, const int32_t* seq_lens,

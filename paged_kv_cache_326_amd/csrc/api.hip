@@ -354,7 +354,7 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* quer
                            int32_t num_seqs, int32_t num_heads, int32_t max_q_len, float scale, hipStream_t stream) {
   const pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
-  if (cache->dtype != PA_F16 && cache->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (cache->dtype != PA_F16 && cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_q_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (!supported_group(num_heads, cache->num_kv_heads)) {
     return (num_heads > 0 && num_heads % cache->num_kv_heads == 0) ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;

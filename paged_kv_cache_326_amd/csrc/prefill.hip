@@ -109,7 +109,13 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   constexpr int KSTEPS = D / 16;         // QK contraction steps
   constexpr int DT = D / 32;             // O^T row tiles
   constexpr int NT = kPW * 64;
-  constexpr int NCHK = kKT * D / 8;      // 16-byte chunks per tile (K, and V)
+  // An FP8 pool's codes are converted to f16 as they are staged in LDS; the
+  // products, the query and the output are f16 then.
+  using CT = typename Src<T>::type;
+  constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
+  constexpr int CE = 16 / Elem<T>::kBytes;  // pool elements per 16-byte chunk
+  static_assert(B % CE == 0, "a chunk of one value row never crosses a block");
+  constexpr int NCHK = kKT * D / CE;     // 16-byte chunks per tile (K, and V)
   constexpr int CPT = (NCHK + NT - 1) / NT;  // per thread
   constexpr int RD = kRing;
   static_assert(RD >= 2, "the prologue stages two tiles from the ring");
@@ -173,7 +179,7 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[KSTEPS];
   {
-    const T* qrow = reinterpret_cast<const T*>(a.query) + (tok * Hq + hq) * D;
+    const CT* qrow = reinterpret_cast<const CT*>(a.query) + (tok * Hq + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
@@ -208,12 +214,12 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   };
 
   // Global -> registers for one tile.  K chunks: key-major (coalesced rows);
-  // V chunks: 8 keys of one dimension from the transposed value tile (a
-  // tile of 32 keys never splits an 8-key piece across blocks, since 8
-  // divides the block size), copied to LDS as they are.  Keys no row of this
-  // workgroup sees (>= kend), or in blocks outside the pool, read as zeros
-  // (their probabilities are zero; a zero V keeps 0 * V finite).
-  // Up to RD tiles are in flight in registers at once.
+  // V chunks: CE keys of one dimension from the transposed value tile (a
+  // tile of 32 keys never splits such a piece across blocks, since CE
+  // divides the block size).  Keys no row of this workgroup sees (>= kend),
+  // or in blocks outside the pool, read as zeros (their probabilities are
+  // zero; a zero V keeps 0 * V finite).  Up to RD tiles are in flight in
+  // registers at once.
   u32x4 kregs[RD][CPT], vregs[RD][CPT];
   auto fetch = [&](u32x4 (&kreg)[CPT], u32x4 (&vreg)[CPT], int t) {
 #pragma unroll
@@ -221,28 +227,36 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       const int c = tid + i * NT;
       if (NCHK % NT != 0 && c >= NCHK) continue;
       {
-        const int key = c / (D / 8), dch = c % (D / 8);
+        const int key = c / (D / CE), dch = c % (D / CE);
         const int pos = t * kKT + key;
         u32x4 x = {0, 0, 0, 0};
         if (pos < kend) {  // keys >= kend are masked for every row of this tile
           const int pb = block_of(pos);
-          if (pb >= 0) x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * 8);
+          if (pb >= 0)
+            x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * CE);
         }
         kreg[i] = x;
       }
       {
-        const int kg = c % (kKT / 8), d = c / (kKT / 8);
-        const int pos = t * kKT + kg * 8;
+        const int kg = c % (kKT / CE), d = c / (kKT / CE);
+        const int pos = t * kKT + kg * CE;
         u32x4 x = {0, 0, 0, 0};
         if (pos < kend) {  // keys >= kend are masked for every row of this tile
           const int pb = block_of(pos);
           if (pb >= 0) {
             x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * D + d) * B + pos % B);
             const int nv = kend - pos;  // keys of this piece that some row sees
-            if (nv < 8) {
+            if (nv < CE) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const uint32_t keep = 2 * e >= nv ? 0u : (2 * e + 1 >= nv ? 0xffffu : 0xffffffffu);
+                uint32_t keep;
+                if constexpr (kFp8) {
+                  keep = 0;
+#pragma unroll
+                  for (int b = 0; b < 4; ++b) keep |= (4 * e + b < nv ? 0xffu : 0u) << (8 * b);
+                } else {
+                  keep = 2 * e >= nv ? 0u : (2 * e + 1 >= nv ? 0xffffu : 0xffffffffu);
+                }
                 x[e] &= keep;
               }
             }
@@ -252,18 +266,36 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       }
     }
   };
+  // Registers -> LDS (as f16 for an FP8 pool: sixteen codes become two
+  // 16-byte pieces, every E4M3 value being exact in f16).
+  auto put = [&](uint16_t* dst, const u32x4& x) {
+    if constexpr (kFp8) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        lo[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e], 1.0f, false));
+        lo[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e], 1.0f, true));
+        hi[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e + 2], 1.0f, false));
+        hi[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e + 2], 1.0f, true));
+      }
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 8) = hi;
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = x;
+    }
+  };
   auto stash = [&](const u32x4 (&kreg)[CPT], const u32x4 (&vreg)[CPT], int st) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (NCHK % NT != 0 && c >= NCHK) continue;
       {
-        const int key = c / (D / 8), dch = c % (D / 8);
-        *reinterpret_cast<u32x4*>(Ks(st) + key * S::kKStride + dch * 8) = kreg[i];
+        const int key = c / (D / CE), dch = c % (D / CE);
+        put(Ks(st) + key * S::kKStride + dch * CE, kreg[i]);
       }
       {
-        const int kg = c % (kKT / 8), d = c / (kKT / 8);
-        *reinterpret_cast<u32x4*>(Vt(st) + d * S::kVStride + kg * 8) = vreg[i];
+        const int kg = c % (kKT / CE), d = c / (kKT / CE);
+        put(Vt(st) + d * S::kVStride + kg * CE, vreg[i]);
       }
     }
   };
@@ -274,7 +306,9 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float qscale = fabsf(a.scale) * kLog2e;
+  // FP8: the staged K values are the codes' values; the pool scale joins
+  // the logit scale (and V's the output factor).
+  const float qscale = fabsf(a.scale) * kLog2e * (kFp8 ? a.cache.k_scale : 1.f);
   // S^T row slot of this lane's A operand, with bits 2 and 3 swapped.
   const int krow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
@@ -286,7 +320,7 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
     const uint16_t* krp = Ks(st) + krow * S::kKStride + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      acc = mfma32<T>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], acc);
+      acc = mfma32<CT>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], acc);
     return acc;
   };
 
@@ -341,9 +375,9 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x0 = pj[8 * ks + 2 * i], x1 = pj[8 * ks + 2 * i + 1];
-        pb[ks][i] = pack2<T>(x0, x1);
+        pb[ks][i] = pack2<CT>(x0, x1);
         if constexpr (std::is_same<T, bf16_t>::value)
-          pl[ks][i] = pack2<T>(x0 - bf16_lo(pb[ks][i]), x1 - bf16_hi(pb[ks][i]));
+          pl[ks][i] = pack2<CT>(x0 - bf16_lo(pb[ks][i]), x1 - bf16_hi(pb[ks][i]));
       }
   };
 
@@ -355,8 +389,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 va = *reinterpret_cast<const u32x4*>(vrp + 16 * ks);
-        o[dt] = mfma32<T>(va, pb[ks], o[dt]);
-        if constexpr (std::is_same<T, bf16_t>::value) o[dt] = mfma32<T>(va, pl[ks], o[dt]);
+        o[dt] = mfma32<CT>(va, pb[ks], o[dt]);
+        if constexpr (std::is_same<T, bf16_t>::value) o[dt] = mfma32<CT>(va, pl[ks], o[dt]);
       }
     }
   };
@@ -417,7 +451,7 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // dimension 32 dt + 8 (j / 4) + 4 hi + j % 4.
   const float l_tot = l_run + shfl_xor(l_run, 32);
   if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (kFp8 ? a.cache.v_scale : 1.f) / l_tot : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (tok * Hq + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -425,8 +459,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       for (int j4 = 0; j4 < 4; ++j4) {
         const int d = 32 * dt + 8 * j4 + 4 * hi;
         u32x2 pk;
-        pk[0] = pack2<T>(o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv);
-        pk[1] = pack2<T>(o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv);
+        pk[0] = pack2<CT>(o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv);
+        pk[1] = pack2<CT>(o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + d) = pk;
       }
   }
@@ -479,6 +513,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   switch (a.cache.dtype) {
     case DType::kF16: return prefill_d<f16_t>(a, G, stream);
     case DType::kBF16: return prefill_d<bf16_t>(a, G, stream);
+    case DType::kFP8: return prefill_d<fp8_t>(a, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
