@@ -274,6 +274,35 @@ def secondary(copies_n: int):
     }
     del cs, pools
     torch.cuda.empty_cache()
+    # The mixed config's chunked prefill over an FP8 pool: the same float16
+    # rows quantised by the library's scatter, codes converted on chip.
+    w = synth.config(5, poison_unused=False, dtype="f16")
+    pre, _ = synth.prefill_decode_split(w)
+    wp = w.subset(pre)
+    cs = _copies(w, copies_n)
+    pf = []
+    for c in cs:
+        kc8, vc8 = harness.fp8_pool_gpu(c, scales)
+        pf.append((harness.GpuWorkload(wp).share_pool(c), kc8, vc8))
+    del cs
+    for g, _, _ in pf:
+        g.key_cache = g.value_cache = None  # the 16-bit pool is no longer needed
+    torch.cuda.empty_cache()
+
+    def fp8_prefill(i):
+        g, kc8, vc8 = pf[i % len(pf)]
+        pa.pa_prefill_chunk(g.out, g.query, kc8, vc8, g.cu_q_lens, g.seq_lens, g.block_tables, wp.scale,
+                            int(wp.q_lens.max()), scales=scales)
+
+    tpf = _median_us(fp8_prefill, iters=20)
+    fl = prefill_flops(wp)
+    res["fp8_e4m3_" + synth.CONFIG_NAMES[5] + "_prefill"] = {
+        "prefill_us": round(tpf, 2), "prefill_flops": fl, "prefill_TFLOPs": round(fl / tpf / 1e6, 1),
+        "prefill_frac_of_mfma_peak": round(fl / tpf / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "vs_bf16_pool": round(res[synth.CONFIG_NAMES[5]]["prefill_us"] / tpf, 3), "scales": list(scales),
+    }
+    del pf
+    torch.cuda.empty_cache()
     return res
 
 
