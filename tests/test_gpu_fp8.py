@@ -240,3 +240,12 @@ def test_fused_append_decode_fp8_matches_separate_calls():
     assert torch.equal(s1, s2)
     assert torch.equal(kc8, kc8b) and torch.equal(vc8, vc8b)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_prefill_fp8_context_beyond_the_staged_table():
+    # More table entries than the workgroup stages in LDS (2505 > 2048).
+    w = synth.custom(seed=34, dtype="f16", num_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
+                     seq_lens=[40070, 50], q_lens=[70, 50], pool_factor=1.02)
+    gw = harness.GpuWorkload(w)
+    kc8, vc8 = harness.fp8_pool_gpu(gw, SCALES[1])
+    _check_prefill(w, gw, kc8, vc8, SCALES[1])

@@ -153,3 +153,19 @@ def test_prefill_growing_logits(dt, slope):
     _sync()
     _, kc, vc, _ = harness.oracle_step(w, seqs=[])
     _check(out, harness.oracle_prefill(w, kc, vc), dt, f"prefill {dt} ramp {slope}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_prefill_context_beyond_the_staged_table(dt):
+    # 40 000 cached tokens at block size 16 need 2505 table entries, more than
+    # the workgroup stages in LDS (2048): the rest are read from the table in
+    # global memory.  A ragged 70-token chunk, plus a short sequence.
+    w = synth.custom(seed=33, dtype=dt, num_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
+                     seq_lens=[40070, 50], q_lens=[70, 50], pool_factor=1.02)
+    gw = harness.GpuWorkload(w)
+    gw.slots()
+    gw.scatter()
+    out = gw.prefill()
+    _sync()
+    _, kc, vc, _ = harness.oracle_step(w, seqs=[])
+    _check(out, harness.oracle_prefill(w, kc, vc), dt, f"prefill {dt} 40k context")
