@@ -144,11 +144,11 @@ struct Src<fp8_t> {
 // Store the VEC = vec16<Src<T>> source elements of one 16-byte chunk (a
 // piece of a key row).
 template <typename T>
-__device__ __forceinline__ void store_chunk(T* dst, const u32x4& data, float) {
+__device__ __forceinline__ void store_chunk(T* dst, const u32x4 data, float) {
   *reinterpret_cast<u32x4*>(dst) = data;
 }
 template <>
-__device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4& data, float scale) {
+__device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4 data, float scale) {
   uint32_t w[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -168,7 +168,7 @@ __device__ __forceinline__ void store_chunk<fp8_t>(fp8_t* dst, const u32x4& data
 // Store the same chunk as one column piece of a transposed value tile:
 // element e goes to p[e * stride].
 template <typename T>
-__device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4& data, float scale) {
+__device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4 data, float scale) {
   if constexpr (Elem<T>::kBytes == 4) {
     uint32_t* q = reinterpret_cast<uint32_t*>(p);
 #pragma unroll
@@ -196,7 +196,7 @@ __device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4& 
 template <typename T>
 __device__ __forceinline__ void store_kv_chunk(T* key_cache, T* value_cache, int which, int64_t blk, int off, int h,
                                                int ch, int vec, int num_kv_heads, int head_dim, int block_size,
-                                               const u32x4& data, float k_scale, float v_scale) {
+                                               const u32x4 data, float k_scale, float v_scale) {
   if (which == 0) {
     T* dst = key_cache + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * vec;
     store_chunk<T>(dst, data, k_scale);
