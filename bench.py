@@ -3,10 +3,9 @@
 
 One step is the whole hot path over one batch: slot mapping of the new
 tokens and their KV scatter into the pool, then decode attention over every
-sequence's paged K/V -- one pa_decode_append call, one launch: the partition
-kernel writes each sequence's new token into its slot and attends, and the
-last partition of each sequence and KV head to finish merges the
-partitions.  The default workload is one
+sequence's paged K/V -- one pa_decode_append call: the partition kernel
+writes each sequence's new token into its slot and attends, the merge
+kernel combines the partitions.  The default workload is one
 LLaMA-2-70B-shaped layer: 16 sequences x 4096 tokens, 64 query / 8 KV heads,
 head_dim 128, fp16, block size 16, a randomly permuted pool of 4096 blocks.
 
@@ -16,13 +15,13 @@ from the 256 MB last-level cache.
 
 Prints one JSON line.  ``value`` is attended KV tokens per second for the
 whole step, from a timed run of plain steps; ``roofline`` reports the
-decode call's algorithmic bytes over the duration of its one launch, the
-partition kernel, from a second timed run of the same steps in which every
-partition kernel records its own start and end into HIP events
+decode call's algorithmic bytes over the duration of its dominant launch,
+the partition kernel, from a second timed run of the same steps in which
+every partition kernel records its own start and end into HIP events
 (hipExtLaunchKernel: no marker packet enters the stream; such self-timed
-launches cost the step a few us, which is why ``value`` is taken from the
-plain run), against 8 TB/s; the decode call alone (no append) is timed
-separately with events around it and reported beside it;
+launches cost the step about 6 us, which is why ``value`` is taken from the
+plain run), against 8 TB/s; the whole decode call, merge included, is
+timed separately and reported beside it;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.
 """
@@ -110,12 +109,7 @@ def write_traffic_record(pmc_dir: str):
     }
     total = 0
     for name, match in (("partition_kernel", part), ("merge_kernel", merge)):
-        try:
-            f, wr = mean("pmc_fetch", match), mean("pmc_write", match)
-        except SystemExit:
-            if name == "merge_kernel":  # merged inside the partition launch
-                continue
-            raise
+        f, wr = mean("pmc_fetch", match), mean("pmc_write", match)
         b = int(round((f * ff + wr * wf) * 1024))
         rec[name] = {"FETCH_SIZE_KiB": round(f, 1), "WRITE_SIZE_KiB": round(wr, 1), "bytes": b}
         total += b
@@ -413,10 +407,9 @@ def main():
     def step(i, ev=None):
         # One decode step: every sequence's new token is written into the
         # pool (slot mapping + scatter) by the partition kernel that owns its
-        # position, which then attends; the last partition of each sequence
-        # and KV head to finish merges.  The kernel (the step's one launch)
-        # records its own start and end into ev[0], ev[1]: no marker packet
-        # enters the stream.
+        # position, which then attends; the merge follows.  The partition
+        # kernel (the dominant launch) records its own start and end into
+        # ev[0], ev[1]: no marker packet enters the stream.
         c = copies[i % len(copies)]
         pa.pa_decode_append(c.out, c.query, c.key_cache, c.value_cache, c.new_key, c.new_value, c.block_tables,
                             c.seq_lens, w.scale, w.max_seq_len, slot_mapping=c.slot_mapping,
@@ -451,8 +444,8 @@ def main():
     torch.cuda.synchronize()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     part_avg_s = float(part_ms.mean()) * 1e-3
-    # The decode call alone (no append), timed apart from the step loop with
-    # events around the call.
+    # The whole decode call (partition kernel, merge and the gap between
+    # them), timed apart from the step loop with events around the call.
     for i in range(5):
         copies[i % len(copies)].decode(partition_size=P, workspace=ws[i % len(copies)])
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
@@ -498,7 +491,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partition_kernel (pa_decode_append: append, attention and merge in one launch)",
+            "kernel": "decode_partition_kernel (pa_decode stage 1)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -160,12 +160,10 @@ pa_status pa_append_kv(const pa_kv_cache* cache, const void* key, const void* va
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                                  int32_t block_size);
 
-/* Bytes of scratch pa_decode needs for sequences longer than one partition:
- * 64 KiB of arrival counters (uint32, one per (sequence, KV head)), then
- * float32 per-partition softmax statistics and partial outputs.
+/* Bytes of float32 scratch pa_decode needs to keep per-partition softmax
+ * statistics and partial outputs of sequences longer than one partition.
  * partition_size 0 means the automatic choice (pass the same value to the
- * decode call).  Returns 0 when no sequence can need more than one
- * partition, and on invalid arguments. */
+ * decode call).  Returns 0 on invalid arguments. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                                  int32_t partition_size);
@@ -187,15 +185,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * max_seq_len   host-side upper bound of seq_lens (<= max_blocks_per_seq *
  *               block_size); longer device values are clamped to it
  * workspace     device scratch of at least pa_decode_workspace_bytes(); may
- *               be NULL when that size is 0.  Its first 64 KiB (the arrival
- *               counters) must be zero before the first call that uses it
- *               (allocate it zero-filled); every call leaves them zero, so
- *               one workspace serves calls of any shapes in stream order.
- *               The rest is overwritten.  Must not overlap out, query or the
- *               cache; calls that share a workspace must not overlap in
- *               time.  The partials of split sequences are merged by the last
- *               partition workgroup of each (sequence, KV head) to finish:
- *               one launch (two when num_seqs * num_kv_heads > 16384).
+ *               be NULL when that size is 0.  Overwritten; must not overlap
+ *               out, query or the cache.
  */
 pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* query,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -211,12 +202,11 @@ pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query,
                        int32_t max_seq_len, float scale, void* workspace,
                        size_t workspace_bytes, int32_t partition_size, hipStream_t stream);
 
-/* pa_decode_ex as two launches, for callers that time or interleave them.
- * stage 1: the partition kernel (writes the output of every sequence that
- * fits one partition and the partials of the others to the workspace, and
- * does not merge them; the counters are not touched); stage 2: the merge of
- * those partials (launches nothing when max_seq_len fits one partition).
- * The result is bit-identical to the one-launch merge.  Arguments as for pa_decode_ex, identical for both
+/* The two launches of pa_decode_ex, for callers that time or interleave
+ * them.  stage 1: the partition kernel (writes the output of every sequence
+ * that fits one partition and the partials of the others to the workspace);
+ * stage 2: the merge of those partials (launches nothing when max_seq_len
+ * fits one partition).  Arguments as for pa_decode_ex, identical for both
  * stages; stage 2 must follow stage 1 on the same stream.  Any other stage
  * value returns PA_ERR_SHAPE. */
 pa_status pa_decode_stage(const pa_kv_cache* cache, void* out, const void* query,
@@ -256,8 +246,7 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* new_key, const 
 
 /* All decode options in one call.  Fields as in pa_decode_ex; the optional
  * ones are NULL / 0 when unused:
- *   stage            0 the whole decode (merge in the partition launch),
- *                    1 the partition kernel alone, 2 the merge kernel
+ *   stage            0 both launches, 1 the partition kernel, 2 the merge
  *   new_key, new_value, slot_mapping   the fused append of pa_decode_append
  *                    (all three or none)
  *   work, num_work   a plan from pa_decode_plan for the same seq_lens,

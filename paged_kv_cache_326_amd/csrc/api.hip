@@ -54,9 +54,6 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Decode workspace: the arrival counters first (a fixed region, so calls of
-// any shapes that share one workspace keep them apart from their partials),
-// then the per-partition maxima, sums and partial outputs.
 struct WsLayout {
   size_t m_off, l_off, o_off, bytes;
 };
@@ -64,8 +61,8 @@ struct WsLayout {
 WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int num_partitions) {
   const size_t rows = (size_t)num_seqs * num_heads * num_partitions;
   WsLayout w;
-  w.m_off = pa::kCounterBytes;
-  w.l_off = w.m_off + align256(rows * 4);
+  w.m_off = 0;
+  w.l_off = align256(rows * 4);
   w.o_off = w.l_off + align256(rows * 4);
   w.bytes = w.o_off + align256(rows * head_dim * 4);
   return w;
@@ -261,10 +258,6 @@ static pa_status decode_run(const pa_decode_args* d, hipStream_t stream) {
     a.ws_m = reinterpret_cast<float*>(base + wl.m_off);
     a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
     a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
-    // One launch unless the caller asked for the two stages separately (or
-    // the batch has more (sequence, KV head) pairs than counters).
-    if (d->stage == 0 && (size_t)num_seqs * cache->num_kv_heads * 4 <= pa::kCounterBytes)
-      a.ws_cnt = reinterpret_cast<uint32_t*>(base);
   }
   const hipError_t e = pa::launch_decode(a, d->stage, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

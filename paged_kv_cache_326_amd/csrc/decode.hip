@@ -42,11 +42,8 @@
 //
 // A sequence that fits one partition is normalised and written directly.
 // Longer sequences write (max, sum, unnormalised o) per partition to the
-// workspace, and the partials are merged,
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// either by the last of the sequence's partition workgroups to finish (one
-// launch; an arrival counter per sequence and KV head) or by a second
-// kernel.
+// workspace and a second kernel merges them:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 #include <math.h>
 
 #include <type_traits>
@@ -147,23 +144,8 @@ constexpr int kMergeBatch = 16;
 // Lazy rescale threshold of the online softmax (log2 units).
 constexpr float kLazy = 8.f;
 
-// Workspace words shared between the workgroups of one launch are written
-// and read as device-scope (agent) atomics: the stores write through to the
-// device's coherence point and the loads read from it, so no cache
-// write-back or invalidate of a whole L2 is needed between them.
-__device__ __forceinline__ void st_shared_ws(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <bool kCoherent>
-__device__ __forceinline__ float ld_ws(const float* p) {
-  if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return *p;
-}
-
 // np partitions of the sequence are merged; rows are num_partitions apart.
-// kCoherent: the partials were written by other workgroups of the same
-// launch (device-scope loads).
-template <int D, bool kCoherent>
+template <int D>
 __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
   const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
   float M = -INFINITY, num = 0.f, den = 0.f;
@@ -173,9 +155,9 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
     for (int i = 0; i < kMergeBatch; ++i) {
       const bool ok = p0 + i < np;
       const int64_t row = row0 + p0 + i;
-      mv[i] = ok ? ld_ws<kCoherent>(a.ws_m + row) : -INFINITY;
-      lv[i] = ok ? ld_ws<kCoherent>(a.ws_l + row) : 0.f;
-      ov[i] = ok ? ld_ws<kCoherent>(a.ws_o + row * D + d) : 0.f;
+      mv[i] = ok ? a.ws_m[row] : -INFINITY;
+      lv[i] = ok ? a.ws_l[row] : 0.f;
+      ov[i] = ok ? a.ws_o[row * D + d] : 0.f;
     }
     float Mb = M;
 #pragma unroll
@@ -553,7 +535,6 @@ decode_partition_kernel(DecodeArgs a) {
 
   // FP8: the widened V values are the codes' values.
   const float vfac = kFp8 ? a.cache.v_scale : 1.f;
-  const bool fused = !direct && a.ws_cnt != nullptr;
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D;
     const int d = idx % D;
@@ -575,13 +556,6 @@ decode_partition_kernel(DecodeArgs a) {
     if (direct) {
       QT* out = reinterpret_cast<QT*>(a.out) + ((int64_t)s * Hq + hq) * D + d;
       store_elem<QT>(out, l > 0.f ? acc / l : 0.f);
-    } else if (fused) {
-      const int64_t row = ((int64_t)s * Hq + hq) * a.num_partitions + part;
-      st_shared_ws(a.ws_o + row * D + d, acc);
-      if (d == 0) {
-        st_shared_ws(a.ws_m + row, Mx);
-        st_shared_ws(a.ws_l + row, l);
-      }
     } else {
       const int64_t row = ((int64_t)s * Hq + hq) * a.num_partitions + part;
       a.ws_o[row * D + d] = acc;
@@ -591,38 +565,13 @@ decode_partition_kernel(DecodeArgs a) {
       }
     }
   }
-  if (!fused) return;
-
-  // 5. Single-launch merge.  Every thread's partial stores complete (they
-  // are device-coherent once counted), then one arrival per workgroup on the
-  // (sequence, KV head) counter; the workgroup that arrives last has every
-  // partition's partials visible, merges them exactly as the merge kernel
-  // does, and puts the counter back to zero for the next call.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // all partials of this workgroup stored; s_m is free
-  const int np = (L + P - 1) / P;
-  int* s_last = reinterpret_cast<int*>(s_m);
-  if (tid == 0) {
-    uint32_t* cnt = a.ws_cnt + (int64_t)s * Hkv + g;
-    const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = before + 1 == (uint32_t)np;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (*s_last == 0) return;
-  for (int idx = tid; idx < G * D; idx += NT) {
-    const int h = idx / D;
-    const int d = idx % D;
-    const int hq = g * G + h;
-    const float v = merge_partials<D, true>(a, s, hq, d, np);
-    store_elem<QT>(reinterpret_cast<QT*>(a.out) + ((int64_t)s * Hq + hq) * D + d, v);
-  }
 }
 
-// Merge kernel for sequences longer than one partition, when the partition
-// kernel does not merge (the two-launch path).  grid (num_heads, num_seqs),
-// D threads.
+// Merge kernel for sequences longer than one partition.  A fused variant
+// (the last workgroup of a sequence and KV head merging after an agent-scope
+// release/acquire on an arrival counter) is correct but on gfx950 every such
+// release writes back the XCD's L2, which cost far more than this launch.
+// grid (num_heads, num_seqs), D threads.
 template <typename T, int D>
 __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
   const int s = blockIdx.y, hq = blockIdx.x, d = threadIdx.x;
@@ -632,7 +581,7 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
   // so the loads need not wait for seq_len; with one, only the sequence's
   // own partitions ran.
   const int np = a.work ? (L + a.partition - 1) / a.partition : a.num_partitions;
-  const float v = merge_partials<D, false>(a, s, hq, d, np);
+  const float v = merge_partials<D>(a, s, hq, d, np);
   if (L <= a.partition) return;  // written directly by the partition kernel
   store_elem<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
 }
@@ -663,7 +612,7 @@ hipError_t launch_typed(const DecodeArgs& a, int stage, hipStream_t stream) {
                                       : launch_partitions<4, T, D, B, G>(a, stream, a.t0, a.t1);
     if (e != hipSuccess) return e;
   }
-  if (stage != 1 && a.max_seq_len > a.partition && a.ws_cnt == nullptr) {
+  if (stage != 1 && a.max_seq_len > a.partition) {
     hipLaunchKernelGGL((decode_reduce_kernel<typename Dec<T>::Q, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
                        stream, a);
     return hipGetLastError();

@@ -44,11 +44,6 @@ struct DecodeArgs {
   float* ws_m;            // [num_seqs][num_heads][num_partitions]
   float* ws_l;            // same
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]
-  // Optional single-launch merge: one arrival counter per (sequence, KV
-  // head), zero on entry and left zero; the last partition workgroup of a
-  // split sequence to arrive merges its partials (else a second kernel
-  // does).
-  uint32_t* ws_cnt;       // [num_seqs][num_kv_heads]
 };
 
 struct PrefillArgs {
@@ -65,10 +60,6 @@ struct PrefillArgs {
 };
 
 constexpr int kMaxPartition = 4096;
-
-// Leading bytes of the decode workspace that hold the arrival counters, at
-// the same place for every call whatever its shapes.
-constexpr size_t kCounterBytes = 65536;
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                                const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,

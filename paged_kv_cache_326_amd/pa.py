@@ -354,20 +354,17 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block
 
 
 def decode_workspace(query, key_cache, max_seq_len: int, partition_size: int = 0) -> torch.Tensor:
-    """Allocate (with torch) the scratch pa_decode needs for these shapes,
-    zero-filled: its leading arrival counters must start at zero (every call
-    leaves them zero, so the workspace can be reused by calls of any shape)."""
+    """Allocate (with torch) the scratch pa_decode needs for these shapes."""
     S, Hq, D = query.shape
     n = pa_decode_workspace_bytes(S, Hq, key_cache.shape[1], D, key_cache.shape[2], max_seq_len, partition_size)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=query.device)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=query.device)
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
               workspace: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None, scales=None,
               stage: int = 0):
-    """Decode attention; ``stage`` 1 or 2 runs only the partition kernel
-    (no merge) or only the merge kernel (pa_decode_stage), 0 the whole decode
-    in one launch (pa_decode_ex)."""
+    """Decode attention; ``stage`` 1 or 2 runs only the partition kernel or
+    only the merge (pa_decode_stage), 0 both (pa_decode_ex)."""
     c = kv_cache(key_cache, value_cache, scales)
     _need(query, "query", io_dtype(key_cache))
     _need(out, "out", io_dtype(key_cache))

@@ -77,12 +77,11 @@ def test_decode_argument_errors(L):
 
 
 def test_workspace_size_formula(L):
-    # 64 KiB of arrival counters, then 4 sequences x 8 heads x ceil(50/16)=4
-    # partitions: m and l rows (float32, 256-byte aligned) plus head_dim floats
-    # per row.
+    # 4 sequences x 8 heads x ceil(50/16)=4 partitions: m and l rows (float32,
+    # 256-byte aligned) plus head_dim floats per row.
     rows = 4 * 8 * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 16) == 65536 + 2 * al(rows * 4) + al(rows * 64 * 4)
+    assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 16) == 2 * al(rows * 4) + al(rows * 64 * 4)
     assert L.pa_decode_workspace_bytes(4, 8, 2, 64, 16, 50, 64) == 0  # one partition: written directly
     # 16 x 8 = 128 pairs: two 2048-token parts each, one workgroup per compute unit
     assert L.pa_decode_auto_partition(16, 8, 4096, 16) == 2048
