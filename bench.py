@@ -44,18 +44,27 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_llama2-70b-bs16x4096_traffic.json")
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_326_amd", "csrc", "decode.hip")
+# The decode kernel's sources: the kernel file and the device helpers it
+# includes (the fused append's stores among them).
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_326_amd", "csrc", f) for f in ("decode.hip", "pa_common.h")]
+
+
+def decode_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the decode partition kernel from the committed
     counter record, or None when the decode kernel source has changed since
     the counters were taken."""
-    import hashlib
-
     try:
         rec = json.load(open(TRAFFIC_RECORD))
-        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+        src = decode_source_digest()
     except (OSError, ValueError):
         return None
     if rec.get("decode_source_sha256") != src:
@@ -73,7 +82,6 @@ def write_traffic_record(pmc_dir: str):
     (KiB per dispatch) scaled by what they read for a plain copy of known
     size, per decode call."""
     import csv
-    import hashlib
 
     from paged_kv_cache_326_amd import synth
 
@@ -117,7 +125,7 @@ def write_traffic_record(pmc_dir: str):
     rec["bytes_per_call"] = total
     rec["algorithmic_bytes_per_call"] = alg
     rec["ratio_to_algorithmic"] = round(total / alg, 4)
-    rec["decode_source_sha256"] = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    rec["decode_source_sha256"] = decode_source_digest()
     with open(TRAFFIC_RECORD, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
