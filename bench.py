@@ -314,6 +314,44 @@ def secondary(copies_n: int):
     return res
 
 
+def prefill_only(steps: int, warmup: int, copies_n: int, fp8: bool):
+    """The mixed config's chunked prefill alone (4 sequences x 512-token
+    chunks over 3584 cached tokens, bf16, or over an FP8 pool built from the
+    same rows as float16), for counter collection on the prefill kernel:
+    one JSON line with its median duration and MFMA rate."""
+    import torch
+    from paged_kv_cache_326_amd import pa, synth
+    from tests import harness
+
+    scales = (0.0173, 0.0291)
+    w = synth.config(5, poison_unused=False, dtype="f16" if fp8 else None)
+    pre, _ = synth.prefill_decode_split(w)
+    wp = w.subset(pre)
+    cs = _copies(w, copies_n)
+    runs = []
+    for c in cs:
+        g = harness.GpuWorkload(wp).share_pool(c)
+        kc, vc = harness.fp8_pool_gpu(c, scales) if fp8 else (c.key_cache, c.value_cache)
+        runs.append((g, kc, vc))
+    del cs
+    torch.cuda.empty_cache()
+
+    def run(i):
+        g, kc, vc = runs[i % len(runs)]
+        pa.pa_prefill_chunk(g.out, g.query, kc, vc, g.cu_q_lens, g.seq_lens, g.block_tables, wp.scale,
+                            int(wp.q_lens.max()), scales=scales if fp8 else None)
+
+    for i in range(warmup):
+        run(i)
+    t = _median_us(run, iters=steps)
+    fl = prefill_flops(wp)
+    return {
+        "workload": synth.CONFIG_NAMES[5] + "_prefill" + ("_fp8_e4m3" if fp8 else ""),
+        "prefill_us": round(t, 2), "prefill_flops": fl, "prefill_TFLOPs": round(fl / t / 1e6, 1),
+        "prefill_frac_of_mfma_peak": round(fl / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4), "steps": steps,
+    }
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """Time the oracle (as it stands) on this host: scatter + decode of the
     whole batch, repeated until `budget_s` has elapsed (at least once)."""
@@ -362,6 +400,8 @@ def main():
     ap.add_argument("--identity-tables", action="store_true", help="unpermuted block layout (indirection overhead)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
+    ap.add_argument("--prefill", choices=("bf16", "fp8"), default=None,
+                    help="time only the mixed config's chunked prefill (for counter collection)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     ap.add_argument("--write-traffic-record", metavar="DIR", default=None,
@@ -398,6 +438,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "copies": args.steps}))
+        return
+
+    if args.prefill:
+        print(json.dumps(prefill_only(args.steps, args.warmup, args.copies, args.prefill == "fp8")), flush=True)
         return
 
     w = synth.config(args.config, poison_unused=False)
