@@ -144,20 +144,23 @@ constexpr int kMergeBatch = 16;
 // Lazy rescale threshold of the online softmax (log2 units).
 constexpr float kLazy = 8.f;
 
-// np partitions of the sequence are merged; rows are num_partitions apart.
+// np partitions of the sequence are merged for dims d .. d+3 of query head
+// hq; rows are num_partitions apart.
 template <int D>
-__device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
+__device__ __forceinline__ f32x4 merge_partials(const DecodeArgs& a, int s, int hq, int d, int np) {
   const int64_t row0 = ((int64_t)s * a.num_heads + hq) * a.num_partitions;
-  float M = -INFINITY, num = 0.f, den = 0.f;
+  float M = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+    float mv[kMergeBatch], lv[kMergeBatch];
+    f32x4 ov[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const bool ok = p0 + i < np;
       const int64_t row = row0 + p0 + i;
       mv[i] = ok ? a.ws_m[row] : -INFINITY;
       lv[i] = ok ? a.ws_l[row] : 0.f;
-      ov[i] = ok ? a.ws_o[row * D + d] : 0.f;
+      ov[i] = ok ? *reinterpret_cast<const f32x4*>(a.ws_o + row * D + d) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float Mb = M;
 #pragma unroll
@@ -165,7 +168,8 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
     if (Mb == -INFINITY) continue;
     if (M != -INFINITY) {
       const float f = fast_exp2(M - Mb);
-      num *= f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) num[k] *= f;
       den *= f;
     }
 #pragma unroll
@@ -173,12 +177,34 @@ __device__ __forceinline__ float merge_partials(const DecodeArgs& a, int s, int 
       // Absent partitions are skipped by select: their l and o are stale.
       const bool live = mv[i] != -INFINITY;
       const float wgt = live ? fast_exp2(mv[i] - Mb) : 0.f;
-      num = live ? fmaf(wgt, ov[i], num) : num;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) num[k] = live ? fmaf(wgt, ov[i][k], num[k]) : num[k];
       den = live ? fmaf(wgt, lv[i], den) : den;
     }
     M = Mb;
   }
-  return den > 0.f ? num / den : 0.f;
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  if (den > 0.f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = num[k] / den;
+  }
+  return r;
+}
+
+// Four consecutive output elements from float32.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<f16_t>(f16_t* p, const f32x4& v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const f32x4& v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // 8-wave workgroups (one per compute unit) keep two steps in flight per
@@ -567,23 +593,26 @@ decode_partition_kernel(DecodeArgs a) {
   }
 }
 
-// Merge kernel for sequences longer than one partition.  A fused variant
-// (the last workgroup of a sequence and KV head merging after an agent-scope
-// release/acquire on an arrival counter) is correct but on gfx950 every such
-// release writes back the XCD's L2, which cost far more than this launch.
-// grid (num_heads, num_seqs), D threads.
-template <typename T, int D>
-__global__ void __launch_bounds__(D) decode_reduce_kernel(DecodeArgs a) {
-  const int s = blockIdx.y, hq = blockIdx.x, d = threadIdx.x;
+// Merge kernel for sequences longer than one partition.  Fused variants (the
+// last partition workgroup of a sequence and KV head merging, after either
+// an agent-scope release/acquire or device-coherent partial stores and an
+// arrival counter) were correct but no faster: every workgroup then waits
+// for its partials to reach memory.  grid (num_kv_heads, num_seqs), one
+// thread per 4 dims of each of the G query heads of the KV head.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(G * D / 4) decode_reduce_kernel(DecodeArgs a) {
+  const int s = blockIdx.y;
+  const int hq = blockIdx.x * G + (int)threadIdx.x / (D / 4);
+  const int d = ((int)threadIdx.x % (D / 4)) * 4;
   int L = a.seq_lens[s];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   // Without a plan every partition wrote its partials or an m = -inf marker,
   // so the loads need not wait for seq_len; with one, only the sequence's
   // own partitions ran.
   const int np = a.work ? (L + a.partition - 1) / a.partition : a.num_partitions;
-  const float v = merge_partials<D>(a, s, hq, d, np);
+  const f32x4 v = merge_partials<D>(a, s, hq, d, np);
   if (L <= a.partition) return;  // written directly by the partition kernel
-  store_elem<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
+  store4<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);
 }
 
 // With events, the kernel's own start and end are recorded into them
@@ -613,8 +642,8 @@ hipError_t launch_typed(const DecodeArgs& a, int stage, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stage != 1 && a.max_seq_len > a.partition) {
-    hipLaunchKernelGGL((decode_reduce_kernel<typename Dec<T>::Q, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<typename Dec<T>::Q, D, G>), dim3(a.cache.num_kv_heads, a.num_seqs),
+                       dim3(G * D / 4), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
