@@ -231,13 +231,19 @@ def secondary(copies_n: int):
     wsd = [pa.decode_workspace(g.query, g.key_cache, wd.max_seq_len) for g in gds]
     tp = _median_us(lambda i: gps[i % len(gps)].prefill(), iters=20)
     td = _median_us(lambda i: gds[i % len(gds)].decode(workspace=wsd[i % len(gds)]))
+    # The step's scatter: slot mapping + reshape_and_cache of all 2096 new
+    # tokens (4 x 512 chunk tokens and 48 decode tokens) in one launch.
+    ta = _median_us(lambda i: cs[i % len(cs)].append())
     fl = prefill_flops(wp)
     nbd = algorithmic_decode_bytes(wd)
+    nba = 4 * w.num_new_tokens * w.num_kv_heads * w.head_dim * w.elem_bytes + 8 * w.num_new_tokens
     res[synth.CONFIG_NAMES[5]] = {
         "prefill_us": round(tp, 2), "prefill_flops": fl, "prefill_TFLOPs": round(fl / tp / 1e6, 1),
         "prefill_frac_of_mfma_peak": round(fl / tp / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_us": round(td, 2), "decode_GBps": round(nbd / td / 1e3, 1),
         "decode_frac_of_hbm_peak": round(nbd / td / 1e3 / HBM_PEAK_GBS, 4), "dtype": w.dtype,
+        "reshape_and_cache_tokens": w.num_new_tokens, "reshape_and_cache_us": round(ta, 2),
+        "reshape_and_cache_bytes": nba, "reshape_and_cache_GBps": round(nba / ta / 1e3, 1),
     }
     del cs, gps, gds, wsd
     torch.cuda.empty_cache()

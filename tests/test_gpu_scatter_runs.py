@@ -1,0 +1,126 @@
+"""The KV scatter's two value-store paths, byte for byte against the oracle's
+scatter: groups of eight consecutive tokens whose slots are consecutive and
+start at a multiple of eight (a prefill chunk inside one block) store whole
+pieces of the transposed value-tile rows; every other group stores each
+value into its column.  Chunks that start off that alignment, cross block
+boundaries, and slot mappings that mix runs, breaks and skipped (-1) slots,
+for every pool type.  GPU only."""
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_326_amd import synth
+
+from tests import harness
+
+pytestmark = pytest.mark.gpu
+
+FP8_SCALES = (0.0173, 0.0291)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    harness.build_if_missing()
+    yield
+    torch.cuda.synchronize()
+
+
+def _pool_bytes(t):
+    import torch
+
+    return t.detach().cpu().contiguous().view(torch.uint8).view(-1).numpy()
+
+
+def _expected(w, slots, dt):
+    """Oracle pool (storage bytes) after scattering the first len(slots) of
+    w's new rows to `slots`."""
+    T = len(slots)
+    nk, nv = w.new_key[:T], w.new_value[:T]
+    if dt == "fp8":
+        kc, vc = oracle.fp8_quantize(w.key_cache, FP8_SCALES[0]), oracle.fp8_quantize(w.value_cache, FP8_SCALES[1])
+        oracle.reshape_and_cache_fp8(kc, vc, nk, nv, slots, *FP8_SCALES)
+    else:
+        kc, vc = w.key_cache.copy(), w.value_cache.copy()
+        oracle.reshape_and_cache(kc, vc, nk, nv, slots)
+    return np.ascontiguousarray(kc).view(np.uint8).reshape(-1), np.ascontiguousarray(vc).view(np.uint8).reshape(-1)
+
+
+def _gpu_pool(gw, dt):
+    if dt == "fp8":
+        return harness.fp8_pool_gpu(gw, FP8_SCALES)
+    return gw.key_cache, gw.value_cache
+
+
+@pytest.mark.parametrize("dt,D,B", [("f16", 128, 16), ("bf16", 128, 32), ("f32", 64, 16), ("fp8", 128, 16),
+                                    ("fp8", 64, 32), ("bf16", 64, 16)])
+def test_append_chunks_aligned_and_not(dt, D, B):
+    # Chunks starting at every alignment (ctx % 8 = 0, 3, 7, ...), lengths
+    # that end mid-group, a chunk crossing several blocks, one-token decodes.
+    from paged_kv_cache_326_amd import pa
+
+    q_lens = [64, 61, 19, 1, 40, 9, 1, 8]
+    ctx = [0, 3, 13, 100, 24, 7, 31, 16]
+    w = synth.custom(seed=411 + D + B, dtype="f16" if dt == "fp8" else dt, num_heads=8, num_kv_heads=4, head_dim=D,
+                     block_size=B, seq_lens=[c + q for c, q in zip(ctx, q_lens)], q_lens=q_lens)
+    gw = harness.GpuWorkload(w)
+    kc, vc = _gpu_pool(gw, dt)
+    pa.pa_append_kv(kc, vc, gw.new_key, gw.new_value, gw.block_tables, gw.seq_lens, gw.cu_q_lens, max(q_lens),
+                    gw.slot_mapping, scales=FP8_SCALES if dt == "fp8" else None)
+    slots = gw.slot_mapping.cpu().numpy()
+    ref_slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
+    np.testing.assert_array_equal(slots, ref_slots)
+    ek, ev = _expected(w, ref_slots, dt)
+    assert np.array_equal(_pool_bytes(kc), ek)
+    assert np.array_equal(_pool_bytes(vc), ev)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32", "fp8"])
+def test_reshape_and_cache_runs_breaks_and_skips(dt):
+    # An explicit slot mapping over 96 tokens: aligned runs of 8 consecutive
+    # slots (whole-piece stores), runs shifted by one, a run with one slot
+    # out of order, runs holding a -1, a trailing partial group.
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    B, D = 16, 128
+    w = synth.custom(seed=512, dtype="f16" if dt == "fp8" else dt, num_heads=8, num_kv_heads=2, head_dim=D,
+                     block_size=B, seq_lens=[96], q_lens=[96], pool_factor=3.0)
+    rng = np.random.default_rng(7)
+    blocks = rng.permutation(w.num_blocks)[:12]
+    slots = np.concatenate([
+        blocks[0] * B + np.arange(8), blocks[0] * B + 8 + np.arange(8),  # two aligned runs in one block
+        blocks[1] * B + 1 + np.arange(8),                                # consecutive but not aligned
+        blocks[2] * B + np.array([0, 1, 2, 3, 5, 4, 6, 7]),              # aligned, one pair swapped
+        blocks[3] * B + np.array([0, 1, 2, -1, 4, 5, 6, 7]),             # a skipped token
+        blocks[4] * B + 8 + np.arange(8),                                # aligned, second half of a block
+        blocks[5] * B + np.arange(8)[::-1],                              # reversed
+        np.full(8, -1),                                                  # all skipped
+        blocks[6] * B + np.arange(8), blocks[7] * B + np.arange(8),      # aligned runs in two blocks
+        blocks[8] * B + 4 + np.arange(8),                                # crosses into the next offset range
+        blocks[9] * B + np.arange(8),
+    ]).astype(np.int64)
+    slots = np.where(slots >= 0, slots, -1)
+    # the out-of-order and shifted runs must not collide with other runs
+    assert len(np.unique(slots[slots >= 0])) == (slots >= 0).sum()
+    T = len(slots)
+    assert T == 96
+    gw = harness.GpuWorkload(w)
+    kc, vc = _gpu_pool(gw, dt)
+    sm = torch.from_numpy(slots).cuda()
+    pa.pa_reshape_and_cache(kc, vc, gw.new_key, gw.new_value, sm, scales=FP8_SCALES if dt == "fp8" else None)
+    ek, ev = _expected(w, slots, dt)
+    assert np.array_equal(_pool_bytes(kc), ek)
+    assert np.array_equal(_pool_bytes(vc), ev)
+    # A trailing partial group (T not a multiple of 8): the first 93 tokens.
+    gw2 = harness.GpuWorkload(w)
+    kc2, vc2 = _gpu_pool(gw2, dt)
+    pa.pa_reshape_and_cache(kc2, vc2, gw2.new_key[:93].contiguous(), gw2.new_value[:93].contiguous(), sm[:93].contiguous(),
+                            scales=FP8_SCALES if dt == "fp8" else None)
+    ek2, ev2 = _expected(w, slots[:93], dt)
+    assert np.array_equal(_pool_bytes(kc2), ek2)
+    assert np.array_equal(_pool_bytes(vc2), ev2)
