@@ -549,7 +549,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partition_kernel (pa_decode stage 1)",
+            "kernel": "decode_partition_kernel of pa_decode_append (new token written, attention over the "
+                      "partition; the merge kernel follows)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
