@@ -19,6 +19,9 @@ Sources (web pages on paged KV caches):
 
 Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   kv_cache_bytes       the worked LLaMA-2-70B values printed on [P1]
+  preallocation_waste  the waste percentages printed on [P1] for requests
+                       against a 4096-slot reservation, and the overflow
+  paged_waste          brute force: at most one partly filled block
   blocks_needed        brute-force count of distinct blocks touched
   slot_mapping         brute-force page-table walk + injectivity/ordering
   reshape_and_cache    round trip, untouched-slot sentinel, skip/duplicate rules
@@ -40,6 +43,8 @@ from .storage import to_float64, round_to_storage  # noqa: F401
 from .paging import (  # noqa: F401
     blocks_needed,
     kv_cache_bytes,
+    preallocation_waste,
+    paged_waste,
     slot_mapping,
     reshape_and_cache,
     gather_kv,

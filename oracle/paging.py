@@ -36,6 +36,31 @@ def kv_cache_bytes(
     return 2 * num_layers * seq_len * num_kv_heads * head_dim * dtype_size * batch_size
 
 
+def preallocation_waste(num_tokens: int, slots: int):
+    """Fraction of a contiguous per-request cache left unused, or None when
+    the request does not fit.
+
+    [P1] "KV Cache 的内存开销与分页机制": a traditional engine reserves the
+    maximum length for every request; the unused share of that reservation
+    is the reserved slots minus the request's tokens, over the reserved
+    slots, and a request longer than the reservation overflows it.
+    """
+    if num_tokens < 0 or slots <= 0:
+        raise ValueError("negative token count or non-positive reservation")
+    if num_tokens > slots:
+        return None
+    return (slots - num_tokens) / slots
+
+
+def paged_waste(num_tokens: int, block_size: int) -> int:
+    """Token slots allocated but unused when a request holds whole blocks.
+
+    [P1] "KV Cache 的内存开销与分页机制": paged allocation hands out
+    fixed-size blocks on demand, so only the last block can be partly empty.
+    """
+    return blocks_needed(num_tokens, block_size) * block_size - num_tokens
+
+
 def slot_mapping(
     block_tables: np.ndarray, seq_lens: np.ndarray, q_lens: np.ndarray, block_size: int
 ) -> np.ndarray:

@@ -159,3 +159,34 @@ def test_storage_round_trip_bf16_and_f16():
     # Known bit patterns: 1.0 = 0x3F80, -2.0 = 0xC000, 1 + 2^-8 ties to even -> 1.0.
     pats = synth.f32_to_storage(np.array([1.0, -2.0, 1 + 2.0**-8, 1 + 3 * 2.0**-8], np.float32), "bf16")
     assert pats.tolist() == [0x3F80, 0xC000, 0x3F80, 0x3F82]
+
+
+def test_preallocation_waste_matches_printed_figures(golden_dir):
+    # The page's waste of a 4096-slot reservation per request (percent, one
+    # decimal as printed) and the overflow of the 8000-token request.
+    g = json.load(open(os.path.join(golden_dir, "preallocation_waste_4096.json")))
+    for row in g["printed"]:
+        w = oracle.preallocation_waste(row["tokens"], g["slots"])
+        if row["waste_percent"] is None:
+            assert w is None
+        else:
+            assert abs(100.0 * w - row["waste_percent"]) < 0.05, (row, w)
+    # The garbled sizes do not reproduce the printed figures.
+    assert abs(100.0 * oracle.preallocation_waste(150, 4096) - 98.8) > 0.05
+    assert abs(100.0 * oracle.preallocation_waste(3200, 4096) - 95.1) > 0.05
+    assert oracle.preallocation_waste(4096, 4096) == 0.0
+    assert oracle.preallocation_waste(0, 4096) == 1.0
+
+
+@pytest.mark.parametrize("B", [1, 16, 32])
+def test_paged_waste_is_less_than_one_block(B):
+    # Brute force: fill blocks token by token; the unused slots are those of
+    # the last, partly filled block only.
+    for n in range(0, 5 * B + 3):
+        blocks, free_in_last = 0, 0
+        for _ in range(n):
+            if free_in_last == 0:
+                blocks, free_in_last = blocks + 1, B
+            free_in_last -= 1
+        assert oracle.paged_waste(n, B) == free_in_last == blocks * B - n
+        assert 0 <= oracle.paged_waste(n, B) < B
