@@ -358,10 +358,14 @@ decode_partition_kernel(DecodeArgs a) {
       const int j = t / B;
       const int pb = (t < ntok && j < nbp) ? s_bt[j] : -1;
       const T* src = kbase + (int64_t)pb * blk_stride + (t % B) * D + CE * grp;
+      // Ordinary loads for K: each instruction reads 64 bytes of 16 key
+      // rows and the next one the other half of the same 128-byte lines,
+      // which the caches then still hold (and a block shared by several
+      // sequences is found there too).  V, read once in whole lines, is
+      // streamed with non-temporal loads.
 #pragma unroll
       for (int ls = 0; ls < NLK; ++ls)
-        b.k[c][ls] = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 4 * CE * ls))
-                             : u32x4{0, 0, 0, 0};
+        b.k[c][ls] = pb >= 0 ? *reinterpret_cast<const u32x4*>(src + 4 * CE * ls) : u32x4{0, 0, 0, 0};
     }
     const int t0 = stok + 8 * grp;
     const int j = t0 / B;
