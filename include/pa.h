@@ -16,12 +16,14 @@
  *
  * KV pool ([P1] "KV Cache 的内存开销与分页机制", fixed-size physical blocks;
  * [P2] section 2.1, one pool preallocated up front).  One layer's pool is two
- * arrays of identical shape
- *     key_cache, value_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ * arrays
+ *     key_cache   : [num_blocks][num_kv_heads][block_size][head_dim]
+ *     value_cache : [num_blocks][num_kv_heads][head_dim][block_size]
  * so that the block_size token vectors of one (block, KV head) are one
  * contiguous tile ([P1] "PagedAttention 的 CUDA Kernel 实现": vectors of a
- * block sit together so that reads coalesce).  A slot numbers token positions
- * in the pool: slot = physical_block * block_size + offset.
+ * block sit together so that reads coalesce); value tiles are stored
+ * transposed (see pa_kv_cache).  A slot numbers token positions in the pool:
+ * slot = physical_block * block_size + offset.
  *
  * Block tables ([P1] "KV Cache 的内存开销与分页机制": one table per request,
  * logical block -> physical block) are int32 [num_seqs][max_blocks_per_seq];
@@ -391,7 +393,11 @@ pa_status pa_scatter_blocks(const pa_kv_cache* cache, const int32_t* block_ids, 
  *                       blocks that are cached for this version are shared
  *                       (taken back from the free list if needed) and
  *                       *num_cached_tokens = their tokens (the caller skips
- *                       their K/V); the rest are fresh.  All or nothing.
+ *                       their K/V); the rest are fresh.  The search stops
+ *                       one token short of the end, so at least the last
+ *                       token is always computed, into a private block (a
+ *                       prompt of k whole cached blocks reuses k - 1).
+ *                       All or nothing.
  * pa_bm_append_token_ids  pa_bm_append_tokens with the new tokens' ids
  *                       (PA_ERR_SHAPE if the sequence's ids are not known;
  *                       pa_bm_append_tokens forgets them)
@@ -456,6 +462,14 @@ int32_t pa_bm_block_size(pa_block_manager* bm);
  *                       capacity scheduled ids (decoding requests in
  *                       admission order, then the newly admitted) and their
  *                       count to *num_scheduled
+ * pa_sched_copies       the copy-on-write pairs of the last
+ *                       pa_sched_schedule call: a scheduled request whose
+ *                       partly filled last block another sequence shares
+ *                       (pa_bm_fork) was given a private block; copy
+ *                       copy_src[i] -> copy_dst[i] with pa_copy_blocks
+ *                       before the step writes its tokens.  Copies up to
+ *                       capacity pairs, returns their number (-1 on bad
+ *                       arguments)
  * pa_sched_step         one token generated by a decoding request
  *                       (PA_ERR_NOT_FOUND for any other id); reaching
  *                       max_tokens finishes it (released by the next
@@ -469,6 +483,7 @@ pa_scheduler* pa_sched_create(pa_block_manager* bm, int32_t max_batch_size);
 void pa_sched_destroy(pa_scheduler* sched);
 pa_status pa_sched_add_request(pa_scheduler* sched, int64_t request_id, int32_t prompt_len, int32_t max_tokens);
 pa_status pa_sched_schedule(pa_scheduler* sched, int64_t* scheduled, int32_t capacity, int32_t* num_scheduled);
+int32_t pa_sched_copies(pa_scheduler* sched, int32_t* copy_src, int32_t* copy_dst, int32_t capacity);
 pa_status pa_sched_step(pa_scheduler* sched, int64_t request_id);
 int32_t pa_sched_state(pa_scheduler* sched, int64_t request_id);
 int32_t pa_sched_generated(pa_scheduler* sched, int64_t request_id);

@@ -26,17 +26,36 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   slot_mapping         brute-force page-table walk + injectivity/ordering
   reshape_and_cache    round trip, untouched-slot sentinel, skip/duplicate rules
   decode_attention     torch SDPA (float64) on an identity-layout pool, closed
-                       forms, block-permutation and shared-prefix invariance
-  prefill_attention    torch SDPA causal / explicit-mask special cases
+                       forms, block-permutation and shared-prefix invariance;
+                       with drop_missing_blocks, SDPA over the dense K/V with
+                       the missing blocks' rows deleted by index
+  prefill_attention    torch SDPA causal / explicit-mask special cases, the
+                       same with missing blocks (mask built from positions),
+                       a row that sees no present key -> zeros, a row that
+                       sees one key -> that key's value
+  copy_blocks          hand-built pools whose values name block and position:
+                       destination = old source, sources and bystanders
+                       untouched, one source to several destinations,
+                       repeated or aliased destinations refused with the
+                       pool intact, out-of-pool and src == dst pairs skipped
+  gather_blocks        rows in id order, out-of-pool rows untouched
+  scatter_blocks       only the named blocks written, repeated id refused,
+                       gather -> wipe -> scatter restores the pool, swap out,
+                       swap in elsewhere and copy back lands the bytes
   BlockPoolModel       FIFO order and conservation of blocks, reference
-                       counts under sharing, brute-force block counts
+                       counts under sharing, brute-force block counts; the
+                       prefix cache against the page's shared-system-prompt
+                       claims, and a prompt of whole cached blocks keeping
+                       its last block private
   SchedulerModel       hand-worked iterations of the three scheduling steps
                        (admission, head-of-line wait, preemption, release),
-                       conservation, batch limit and block-need invariants
+                       conservation, batch limit and block-need invariants,
+                       a forked request's copy-on-write pair worked by hand
   fp8 (E4M3 codes)     torch float8_e4m3fn values and rounding, hand-worked
                        values, exact midpoints, brute-force nearest,
                        saturation and quantisation error bounds
-No function here is "parity unpinned".
+Every function above has at least one pin that does not come from the
+oracle itself; none is "parity unpinned".
 """
 
 from .storage import to_float64, round_to_storage  # noqa: F401

@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paging import gather_kv
+from .paging import gather_kv, gather_kv_present
 
 
 def _attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -34,6 +34,7 @@ def decode_attention(
     block_tables: np.ndarray,
     seq_lens: np.ndarray,
     scale: float,
+    drop_missing_blocks: bool = False,
 ) -> np.ndarray:
     """One new token per sequence attends over all of that sequence's cached
     tokens (its own included), read through the block table.
@@ -44,6 +45,9 @@ def decode_attention(
     where the vectors are read from ([P1] "PagedAttention 的 CUDA Kernel 实现").
 
     query [S, Hq, D], caches [NB, Hkv, B, D], all float64.  Returns [S, Hq, D].
+    With ``drop_missing_blocks`` a table entry outside the pool contributes
+    no keys (the library's contract for such entries); a sequence left with
+    no key yields zeros.  Without it such an entry raises.
     """
     S, Hq, D = query.shape
     Hkv = key_cache.shape[1]
@@ -53,7 +57,12 @@ def decode_attention(
         L = int(seq_lens[s])
         if L == 0:
             continue
-        K, V = gather_kv(key_cache, value_cache, block_tables[s], L)
+        if drop_missing_blocks:
+            K, V, _ = gather_kv_present(key_cache, value_cache, block_tables[s], L)
+            if len(K) == 0:
+                continue
+        else:
+            K, V = gather_kv(key_cache, value_cache, block_tables[s], L)
         for h in range(Hq):
             g = h // G
             out[s, h] = _attend(query[s, h], K[:, g, :], V[:, g, :], scale)
@@ -68,6 +77,7 @@ def prefill_attention(
     block_tables: np.ndarray,
     seq_lens: np.ndarray,
     scale: float,
+    drop_missing_blocks: bool = False,
 ) -> np.ndarray:
     """A chunk of new tokens per sequence attends causally over the cache.
 
@@ -78,6 +88,9 @@ def prefill_attention(
     attends to positions 0 .. ctx + i.
 
     query [T, Hq, D] float64 with T = cu_q_lens[-1].  Returns [T, Hq, D].
+    ``drop_missing_blocks`` as in decode_attention: the positions of a
+    missing block hold no key; the rest keep their causal visibility, and a
+    row that sees no key yields zeros.
     """
     T, Hq, D = query.shape
     Hkv = key_cache.shape[1]
@@ -90,13 +103,20 @@ def prefill_attention(
         if q == 0:
             continue
         ctx = L - q
-        K, V = gather_kv(key_cache, value_cache, block_tables[s], L)
+        if drop_missing_blocks:
+            K, V, pos = gather_kv_present(key_cache, value_cache, block_tables[s], L)
+        else:
+            K, V = gather_kv(key_cache, value_cache, block_tables[s], L)
+            pos = np.arange(L)
         for h in range(Hq):
             g = h // G
             Kh, Vh = K[:, g, :], V[:, g, :]
-            Z = scale * (query[t0:t1, h, :] @ Kh.T)  # [q, L]
-            visible = np.arange(L)[None, :] <= (ctx + np.arange(q))[:, None]
-            Z = np.where(visible, Z, -np.inf)
+            Z = scale * (query[t0:t1, h, :] @ Kh.T)  # [q, number of keys]
+            visible = pos[None, :] <= (ctx + np.arange(q))[:, None]
+            rows = visible.any(axis=1)  # a row that sees no key stays zero
+            if not rows.any():
+                continue
+            Z = np.where(visible[rows], Z[rows], -np.inf)
             P = np.exp(Z - Z.max(axis=1, keepdims=True))
-            out[t0:t1, h, :] = (P @ Vh) / P.sum(axis=1, keepdims=True)
+            out[t0:t1, h, :][rows] = (P @ Vh) / P.sum(axis=1, keepdims=True)
     return out

@@ -30,6 +30,8 @@ involved at all: the library's hashed lookup must behave exactly like it.
 
 from collections import deque
 
+import numpy as np
+
 from .paging import blocks_needed
 
 
@@ -87,11 +89,17 @@ class BlockPoolModel:
         self.version[sid] = 0
 
     def add_sequence_tokens(self, sid, ids, version=0):
-        """Returns how many leading tokens were found cached."""
+        """Returns how many leading tokens were found cached.
+
+        Lookups stop one token short of the end: the prompt's last token is
+        always computed (its logits start generation), so the block holding
+        it must be private, never a shared cached block.  A prompt that is a
+        whole number of cached blocks therefore reuses all but its last
+        block."""
         assert sid not in self.tables
         ids, B = [int(x) for x in ids], self.block_size
         hits = []
-        for i in range(len(ids) // B):
+        for i in range(max(len(ids) - 1, 0) // B):
             b = self.cached.get((version, tuple(ids[: (i + 1) * B])))
             if b is None:
                 break
@@ -167,14 +175,65 @@ class BlockPoolModel:
         del self.lengths[sid], self.ids[sid], self.version[sid]
 
 
+def _in_pool(b, num_blocks):
+    return 0 <= int(b) < num_blocks
+
+
 def copy_blocks(pool, src, dst):
-    """Pool block src[i] -> pool block dst[i] for each pair, in place."""
-    pool[list(dst)] = pool[list(src)]
+    """Pool block src[i] -> pool block dst[i] for each pair, in place.
+
+    [P1] "KV Cache 的内存开销与分页机制" and [P2] section 4.1: sequences share
+    physical blocks; a sequence about to write into a shared block first
+    gets a private copy of it.  ``pool`` is one pool array whose first axis
+    numbers the blocks (the key pool or the value pool: the per-block layout
+    does not matter to a copy).
+
+    Contract (the library's): a pair with an id outside the pool, or with
+    src == dst, is skipped; among the remaining pairs no destination may
+    repeat and no destination may also be a source, so the result does not
+    depend on the order of the copies.  A violation raises ValueError and
+    leaves the pool unchanged.
+    """
+    src, dst = [int(x) for x in src], [int(x) for x in dst]
+    if len(src) != len(dst):
+        raise ValueError("src and dst differ in length")
+    nb = pool.shape[0]
+    pairs = [(a, b) for a, b in zip(src, dst) if _in_pool(a, nb) and _in_pool(b, nb) and a != b]
+    dsts = [b for _, b in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block repeats")
+    if set(dsts) & {a for a, _ in pairs}:
+        raise ValueError("a destination block is also a source")
+    for a, b in pairs:
+        pool[b] = pool[a].copy()
 
 
-def gather_blocks(pool, ids):
-    return pool[list(ids)].copy()
+def gather_blocks(pool, ids, out=None):
+    """Pool block ids[i] -> row i of a staging array (swap out).
+
+    [P2] section 3: blocks are moved out of device memory and back.  Rows
+    of ids outside the pool are left as they are (zeros when ``out`` is not
+    given).
+    """
+    ids = [int(x) for x in ids]
+    nb = pool.shape[0]
+    if out is None:
+        out = np.zeros((len(ids),) + pool.shape[1:], dtype=pool.dtype)
+    for i, b in enumerate(ids):
+        if _in_pool(b, nb):
+            out[i] = pool[b]
+    return out
 
 
 def scatter_blocks(pool, ids, rows):
-    pool[list(ids)] = rows
+    """Row i of a staging array -> pool block ids[i], in place (swap in).
+    Ids outside the pool are skipped; a repeated id raises ValueError (the
+    result would depend on the order of the writes)."""
+    ids = [int(x) for x in ids]
+    nb = pool.shape[0]
+    live = [b for b in ids if _in_pool(b, nb)]
+    if len(set(live)) != len(live):
+        raise ValueError("a destination block repeats")
+    for i, b in enumerate(ids):
+        if _in_pool(b, nb):
+            pool[b] = rows[i]

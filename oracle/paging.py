@@ -116,6 +116,30 @@ def reshape_and_cache(
         value_cache[block, :, :, offset] = value[t]
 
 
+def gather_kv_present(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndarray, seq_len: int):
+    """K, V [n, num_kv_heads, head_dim] and positions [n] of the tokens of one
+    sequence whose table entry names a block inside the pool.
+
+    The library's contract for a table entry outside [0, num_blocks) (a
+    missing block): its positions hold no key, so they are left out of the
+    attention entirely, as if the sequence had no token there; the other
+    tokens keep their positions (and so their causal visibility).  Built
+    token by token from the definition of the table walk.
+    """
+    B, nb = key_cache.shape[2], key_cache.shape[0]
+    ks, vs, pos = [], [], []
+    for t in range(seq_len):
+        phys = int(table_row[t // B])
+        if 0 <= phys < nb:
+            ks.append(key_cache[phys, :, t % B, :])
+            vs.append(value_cache[phys, :, :, t % B])
+            pos.append(t)
+    Hkv, D = key_cache.shape[1], key_cache.shape[3]
+    if not pos:
+        return np.zeros((0, Hkv, D)), np.zeros((0, Hkv, D)), np.zeros(0, dtype=np.int64)
+    return np.stack(ks), np.stack(vs), np.asarray(pos, dtype=np.int64)
+
+
 def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndarray, seq_len: int):
     """Contiguous K and V [seq_len, num_kv_heads, head_dim] of one sequence.
 
@@ -127,6 +151,8 @@ def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndar
     B = key_cache.shape[2]
     n = blocks_needed(seq_len, B)
     phys = np.asarray(table_row[:n], dtype=np.int64)
+    if ((phys < 0) | (phys >= key_cache.shape[0])).any():
+        raise ValueError("a table entry names a block outside the pool")
     # Logical order is block-major, offset-minor:
     # keys [n, Hkv, B, D] -> [n, B, Hkv, D]; values [n, Hkv, D, B] -> [n, B, Hkv, D].
     K = key_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, key_cache.shape[1], key_cache.shape[3])

@@ -33,6 +33,7 @@ class SchedulerModel:
         self.waiting = deque()
         self.active = []  # admission order
         self.req = {}     # id -> dict(prompt, max_tokens, generated, state)
+        self.copies = []  # copy-on-write (old, new) pairs of the last schedule()
 
     def add_request(self, rid, prompt_len, max_tokens):
         if prompt_len < 0 or max_tokens < 1:
@@ -45,6 +46,7 @@ class SchedulerModel:
     def schedule(self):
         B = self.pool.block_size
         scheduled = []
+        self.copies = []
         # Step 1: decoding requests.
         for rid in self.active:
             r = self.req[rid]
@@ -58,7 +60,9 @@ class SchedulerModel:
             grow = tokens - self.pool.lengths[rid]
             if grow > 0:
                 try:
-                    self.pool.append_tokens(rid, grow)
+                    # A shared, partly filled last block (a forked request)
+                    # is replaced by a private one: the pair is reported.
+                    self.copies += self.pool.append_tokens(rid, grow)
                 except NoBlocks:
                     continue
             scheduled.append(rid)

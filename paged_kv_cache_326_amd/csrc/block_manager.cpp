@@ -247,12 +247,16 @@ pa_status pa_bm_add_sequence_tokens(pa_block_manager* m, int64_t seq_id, const i
   if (m->seqs.count(seq_id)) return PA_ERR_EXISTS;
   const int32_t B = m->block_size;
   const int64_t need = blocks_for(num_tokens, B);
-  // Leading full blocks already cached for this version and prefix.
+  // Leading full blocks already cached for this version and prefix.  The
+  // search stops one token short of the end: the prompt's last token is
+  // always computed (its logits start generation), so the block it lies in
+  // must be private, never a shared cached block.
   std::vector<int32_t> hits;
   int64_t revived = 0;
   int32_t parent = -1;
   uint64_t ph = 0;
-  for (int64_t i = 0; i < num_tokens / B; ++i) {
+  const int64_t searchable = num_tokens > 0 ? (num_tokens - 1) / B : 0;
+  for (int64_t i = 0; i < searchable; ++i) {
     const int32_t* t = token_ids + i * B;
     const uint64_t h = block_hash(m, ph, version, t);
     const int32_t c = lookup(m, h, version, parent, t);

@@ -437,8 +437,7 @@ decode_partition_kernel(DecodeArgs a) {
     float mx = z[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = max_across_rows(mx);  // the four k groups of head r
     // The reference maximum moves only when the step exceeds it by more
     // than kLazy (log2 units), so probabilities stay below 2^kLazy and the
     // accumulator rescale is rare; the final division by the sum cancels
@@ -549,8 +548,7 @@ decode_partition_kernel(DecodeArgs a) {
 
   // 4. The wave's partials -> LDS, then merge the waves.  Lane (head r,
   // group grp) holds dims 16*dd + 4*grp + jj; the four groups' sums add up.
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+  const float l_tot = sum_across_rows(l_run);
   if (r < G) {
 #pragma unroll
     for (int dd = 0; dd < NDT; ++dd)

@@ -99,20 +99,6 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (r - (120u << 3));
 }
 
-// Unpack one 32-bit word holding two storage elements (or one f32) to floats.
-template <typename T>
-__device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b);
-template <>
-__device__ __forceinline__ void unpack2<f16_t>(uint32_t w, float& a, float& b) {
-  a = f16_lo(w);
-  b = f16_hi(w);
-}
-template <>
-__device__ __forceinline__ void unpack2<bf16_t>(uint32_t w, float& a, float& b) {
-  a = bf16_lo(w);
-  b = bf16_hi(w);
-}
-
 // Store one float as a storage element.
 template <typename T>
 __device__ __forceinline__ void store_elem(T* p, float x);
@@ -207,31 +193,32 @@ __device__ __forceinline__ void store_kv_chunk(T* key_cache, T* value_cache, int
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane moves.  DPP works inside 16-lane rows; the controls used here:
-//   quad_perm xor 1 / xor 2  (within groups of 4 lanes)
-//   row_half_mirror          (lane i <-> 7 - i inside each group of 8)
-//   row_ror:8                (lane i <-> i ^ 8 inside each row of 16)
+// Cross-lane reductions over the four 16-lane rows of a wave, on the vector
+// ALU (no LDS round trip).  v_permlane16_swap with both operands x swaps the
+// odd rows of one copy with the even rows of the other, so the two results
+// hold rows (0, 0, 2, 2) and (1, 1, 3, 3): combining them pairs row 0 with
+// row 1 and row 2 with row 3.  v_permlane32_swap does the same for the two
+// 32-lane halves.
 // ---------------------------------------------------------------------------
-enum : int {
-  kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
-  kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
-  kDppHalfMirror = 0x141,   // row_half_mirror
-  kDppRowRor8 = 0x128,      // row_ror:8
-};
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float shfl_xor(float x, int mask) {
-  return __shfl_xor(x, mask, 64);
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
-  return x;
+// Maximum (sum) of x over the lanes l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float max_across_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_across_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_across_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

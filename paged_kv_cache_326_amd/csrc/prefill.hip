@@ -94,15 +94,6 @@ struct PrefillSmem {
   static constexpr int kBytes = kStages * kStage * 2;
 };
 
-// max(x, x of the lane 32 away): one v_permlane32_swap exchanges the upper
-// half of the first operand with the lower half of the second, so with both
-// operands x each lane holds its own value in one result and its partner's
-// in the other.
-__device__ __forceinline__ float max_across_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 template <typename T, int D, int B, int G>
 __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2))) prefill_kernel(PrefillArgs a) {
   constexpr int QP = kRows / G;          // positions per workgroup
@@ -138,9 +129,12 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   const int s = u / nqt / a.cache.num_kv_heads;
 
   const int qbeg = a.cu_q_lens[s];
-  const int q_len = a.cu_q_lens[s + 1] - qbeg;
+  // Rows stay below the call's token count (the query and output length),
+  // whatever the other prefix sums hold.
+  const int qend = min(a.cu_q_lens[s + 1], a.cu_q_lens[a.num_seqs]);
+  const int q_len = qend - qbeg;
   const int q0 = qt * QP;
-  if (q0 >= q_len) return;
+  if (qbeg < 0 || q0 >= q_len) return;
   int L = a.seq_lens[s];
   const int Lmax = a.max_blocks * B;
   L = L > Lmax ? Lmax : L;
@@ -332,14 +326,19 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // probabilities are taken against the moved maximum and the accumulator
   // rescale (rare) is left to the caller through alpha.
   u32x4 pb[2], pl[2];
-  auto softmax = [&](f32x16 sc, int t, bool masked, float& alpha) {
+  // `gaps` bit h (h = 0, 1): keys 16h .. 16h+15 of the tile lie in a block
+  // missing from the pool (table entry outside it).  Such keys hold no
+  // vector, so they are masked like keys past the diagonal, never read as
+  // zeros (a zero key would still add to the row's normaliser).
+  auto softmax = [&](f32x16 sc, int t, bool masked, uint32_t gaps, float& alpha) {
     float mt = -INFINITY;
     if (masked) {
       const int kt0 = t * kKT + 8 * hi;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = kt0 + 16 * (j >> 3) + (j & 7);
-        sc[j] = key <= limit ? sc[j] * qscale : -INFINITY;
+        const bool gone = (gaps >> (j >> 3)) & 1u;
+        sc[j] = key <= limit && !gone ? sc[j] * qscale : -INFINITY;
         mt = fmaxf(mt, sc[j]);
       }
     } else {
@@ -423,12 +422,15 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
         const int st2 = st1 == 2 ? 0 : st1 + 1;
         float alpha;
         f32x16 sn;
-        if (t * kKT + kKT - 1 > lim_min) {
+        // Wave-uniform: the tile's two 16-key halves each lie in one block.
+        const uint32_t gaps = __builtin_amdgcn_readfirstlane((block_of(t * kKT) < 0 ? 1u : 0u) |
+                                                             (block_of(t * kKT + 16) < 0 ? 2u : 0u));
+        if (t * kKT + kKT - 1 > lim_min || gaps) {
           sn = scores(st1);
-          softmax(sc, t, true, alpha);
+          softmax(sc, t, true, gaps, alpha);
         } else {
           sn = scores(st1);
-          softmax(sc, t, false, alpha);
+          softmax(sc, t, false, 0u, alpha);
         }
         if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -449,7 +451,7 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
 
   // Normalise and store this lane's row: accumulator j of tile dt is
   // dimension 32 dt + 8 (j / 4) + 4 hi + j % 4.
-  const float l_tot = l_run + shfl_xor(l_run, 32);
+  const float l_tot = sum_across_halves(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? (kFp8 ? a.cache.v_scale : 1.f) / l_tot : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (tok * Hq + hq) * D;

@@ -53,6 +53,10 @@ struct pa_scheduler {
   std::unordered_map<int64_t, Request> reqs;  // waiting and active requests
   std::deque<int64_t> waiting;                // FIFO
   std::vector<int64_t> active;                // admission order
+  // Copy-on-write pairs of the last pa_sched_schedule call: a scheduled
+  // request whose partly filled last block is shared (pa_bm_fork) received
+  // a private block; the caller copies old -> new before the step's scatter.
+  std::vector<int32_t> copy_src, copy_dst;
 };
 
 extern "C" {
@@ -85,6 +89,8 @@ pa_status pa_sched_schedule(pa_scheduler* s, int64_t* scheduled, int32_t capacit
   if (!s || !num_scheduled || (capacity > 0 && !scheduled)) return PA_ERR_NULL;
   std::lock_guard<std::mutex> g(s->mu);
   std::vector<int64_t> out;
+  s->copy_src.clear();
+  s->copy_dst.clear();
 
   // 1. Decoding requests: one more block when their tokens outgrow the
   // blocks they own, or preemption for this iteration.
@@ -101,6 +107,10 @@ pa_status pa_sched_schedule(pa_scheduler* s, int64_t* scheduled, int32_t capacit
       const pa_status st = pa_bm_append_tokens(s->bm, id, (int32_t)(tokens - have), &src, &dst, &ncopy);
       if (st == PA_ERR_NO_BLOCKS) continue;  // preempted
       if (st != PA_OK) return st;
+      if (ncopy > 0) {
+        s->copy_src.push_back(src);
+        s->copy_dst.push_back(dst);
+      }
     }
     out.push_back(id);
   }
@@ -136,6 +146,17 @@ pa_status pa_sched_schedule(pa_scheduler* s, int64_t* scheduled, int32_t capacit
   *num_scheduled = (int32_t)out.size();
   for (int32_t i = 0; i < capacity && i < (int32_t)out.size(); ++i) scheduled[i] = out[i];
   return PA_OK;
+}
+
+int32_t pa_sched_copies(pa_scheduler* s, int32_t* copy_src, int32_t* copy_dst, int32_t capacity) {
+  if (!s || (capacity > 0 && (!copy_src || !copy_dst))) return -1;
+  std::lock_guard<std::mutex> g(s->mu);
+  const int32_t n = (int32_t)s->copy_src.size();
+  for (int32_t i = 0; i < capacity && i < n; ++i) {
+    copy_src[i] = s->copy_src[i];
+    copy_dst[i] = s->copy_dst[i];
+  }
+  return n;
 }
 
 pa_status pa_sched_step(pa_scheduler* s, int64_t id) {

@@ -26,6 +26,7 @@ if hasattr(torch, "float8_e4m3fn"):
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH",
            6: "PA_ERR_NO_BLOCKS", 7: "PA_ERR_NOT_FOUND", 8: "PA_ERR_EXISTS"}
 PA_ERR_SHAPE = 2
+PA_ERR_WORKSPACE = 4
 PA_ERR_NO_BLOCKS = 6
 PA_ERR_NOT_FOUND = 7
 PA_ERR_EXISTS = 8
@@ -119,6 +120,7 @@ EXPORTS = (
     "pa_sched_destroy",
     "pa_sched_add_request",
     "pa_sched_schedule",
+    "pa_sched_copies",
     "pa_sched_step",
     "pa_sched_state",
     "pa_sched_generated",
@@ -224,6 +226,8 @@ def lib() -> ctypes.CDLL:
     L.pa_sched_add_request.restype = ctypes.c_int
     L.pa_sched_schedule.argtypes = [sc, vp, i32, vp]
     L.pa_sched_schedule.restype = ctypes.c_int
+    L.pa_sched_copies.argtypes = [sc, vp, vp, i32]
+    L.pa_sched_copies.restype = i32
     L.pa_sched_step.argtypes = [sc, i64]
     L.pa_sched_step.restype = ctypes.c_int
     for name in ("pa_sched_state", "pa_sched_generated"):
@@ -701,6 +705,16 @@ class Scheduler:
         buf = (ctypes.c_int64 * cap)()
         _check(L.pa_sched_schedule(self._h, buf, cap, ctypes.addressof(n)), "pa_sched_schedule")
         return list(buf[: n.value])
+
+    def copies(self):
+        """Copy-on-write (old, new) block pairs of the last schedule() call."""
+        L = lib()
+        n = L.pa_sched_copies(self._h, None, None, 0)
+        if n <= 0:
+            return []
+        src, dst = (ctypes.c_int32 * n)(), (ctypes.c_int32 * n)()
+        L.pa_sched_copies(self._h, src, dst, n)
+        return list(zip(src, dst))
 
     def step(self, request_id: int):
         _check(lib().pa_sched_step(self._h, int(request_id)), "pa_sched_step")

@@ -20,6 +20,13 @@ UNIT_ROUNDOFF = {"f32": 2.0**-24, "f16": 2.0**-11, "bf16": 2.0**-8}
 ATOL = RTOL = 2e-3
 
 
+# Parity margins of the comparisons made in this process: one record per
+# tolerance_ok call (the test that made it, the dtype, the largest error and
+# the largest err / bound under the bar used and under the plain 2e-3 +
+# 2e-3 |ref| bar).  tests/conftest.py prints them at the end of the session.
+MARGINS: list = []
+
+
 def tolerance_ok(got64: np.ndarray, ref64: np.ndarray, dtype: str):
     """|got - ref| <= ATOL + (RTOL + u_dtype) |ref| elementwise.
 
@@ -28,8 +35,20 @@ def tolerance_ok(got64: np.ndarray, ref64: np.ndarray, dtype: str):
     """
     err = np.abs(got64 - ref64)
     bound = ATOL + (RTOL + UNIT_ROUNDOFF[dtype]) * np.abs(ref64)
+    plain = ATOL + RTOL * np.abs(ref64)
     bad = ~(err <= bound)  # NaN counts as bad
-    return (not bad.any()), float(np.nanmax(err) if err.size else 0.0), int(bad.sum())
+    maxerr = float(np.nanmax(err) if err.size else 0.0)
+    if err.size:
+        MARGINS.append({
+            "test": os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0],
+            "dtype": dtype,
+            "n": int(err.size),
+            "max_abs_err": maxerr,
+            "max_err_over_bound": float(np.nanmax(err / bound)),
+            "max_err_over_plain_bound": float(np.nanmax(err / plain)),
+            "n_outside_plain_bound": int((~(err <= plain)).sum()),
+        })
+    return (not bad.any()), maxerr, int(bad.sum())
 
 
 def build_if_missing():

@@ -381,3 +381,34 @@ def test_decode_growing_logits(dt, slope, partition):
     _sync()
     _, _, _, ref = harness.oracle_step(w)
     _assert_close(_as64(out, w.dtype), ref, w.dtype, f"decode {dt} ramp {slope} P={partition}")
+
+
+@pytest.mark.parametrize("dt,G,P", [("f16", 8, 0), ("bf16", 4, 32), ("f32", 2, 16)])
+def test_decode_skips_table_entries_outside_the_pool(dt, G, P):
+    # The library skips a table entry outside [0, num_blocks): its positions
+    # hold no key.  Entries -1 and num_blocks + 3 are planted after the step's
+    # tokens are written (one sequence loses every block); the oracle drops
+    # the same keys.  Missing blocks' slots are NaN-poisoned in the pool, so a
+    # kernel that read them would fail.
+    import torch
+
+    w = synth.custom(seed=41, dtype=dt, num_heads=2 * G, num_kv_heads=2, head_dim=128, block_size=16,
+                     seq_lens=[70, 300, 33, 129], pool_factor=1.5)
+    gw = harness.GpuWorkload(w)
+    gw.slots()
+    gw.scatter()
+    _, kc, vc, _ = harness.oracle_step(w, seqs=[])
+    tables = w.block_tables.copy()
+    tables[0, 1] = -1
+    tables[1, 2] = w.num_blocks + 3
+    tables[1, 10] = -7
+    tables[2, :3] = -1
+    tables[3, 8] = -1  # the last (one-token) block
+    gw.block_tables = torch.from_numpy(tables).cuda()
+    out = gw.decode(partition_size=P)
+    _sync()
+    q = oracle.to_float64(w.query, dt)
+    ref = oracle.decode_attention(q, kc, vc, tables, w.seq_lens, w.scale, drop_missing_blocks=True)
+    got = _as64(out, dt)
+    assert (got[2] == 0).all()
+    _assert_close(got, ref, dt, f"decode with missing blocks {dt} G={G} P={P}")

@@ -169,3 +169,31 @@ def test_prefill_context_beyond_the_staged_table(dt):
     _sync()
     _, kc, vc, _ = harness.oracle_step(w, seqs=[])
     _check(out, harness.oracle_prefill(w, kc, vc), dt, f"prefill {dt} 40k context")
+
+
+@pytest.mark.parametrize("dt,B", [("bf16", 16), ("f16", 32)])
+def test_prefill_skips_table_entries_outside_the_pool(dt, B):
+    # Entries outside [0, num_blocks) in the cached prefix and inside the
+    # chunk, planted after the chunk's K/V are written: those positions hold
+    # no key (masked, not read as zeros); the other keys keep their causal
+    # visibility.  Sequence 1's first block is missing, so its first rows
+    # see no key at all until the chunk reaches the next block.
+    import torch
+
+    w = synth.custom(seed=43, dtype=dt, num_heads=8, num_kv_heads=2, head_dim=128, block_size=B,
+                     seq_lens=[700, 90, 400], q_lens=[300, 90, 64], pool_factor=1.3)
+    gw = harness.GpuWorkload(w)
+    gw.slots()
+    gw.scatter()
+    _, kc, vc, _ = harness.oracle_step(w, seqs=[])
+    tables = w.block_tables.copy()
+    tables[0, 2] = -1
+    tables[0, 500 // B] = w.num_blocks
+    tables[1, 0] = -1
+    tables[2, 5] = -3
+    gw.block_tables = torch.from_numpy(tables).cuda()
+    out = gw.prefill()
+    _sync()
+    q = oracle.to_float64(w.query, dt)
+    ref = oracle.prefill_attention(q, w.cu_q_lens, kc, vc, tables, w.seq_lens, w.scale, drop_missing_blocks=True)
+    _check(out, ref, dt, f"prefill with missing blocks {dt} B={B}")

@@ -181,3 +181,88 @@ def test_tiny_config_end_to_end_is_finite_and_ignores_poison():
     out = oracle.decode_attention(oracle.to_float64(w.query, w.dtype), kc, vc, w.block_tables, w.seq_lens, w.scale)
     assert out.shape == (4, 8, 64) and np.isfinite(out).all()
     assert np.abs(out).max() < 3.0
+
+
+# ---- table entries outside the pool (missing blocks) -------------------------
+
+
+def _missing_case(B=8, Hq=4, Hkv=2, D=16, seed=31):
+    rng = np.random.default_rng(seed)
+    S, nbk = 3, 5
+    L = nbk * B
+    Kd = rng.standard_normal((S, L, Hkv, D))
+    Vd = rng.standard_normal((S, L, Hkv, D))
+    kc, vc, tables = _identity_pool(Kd, Vd, B)
+    nb = kc.shape[0]
+    tables = tables.copy()
+    tables[0, 1] = -1        # sequence 0 loses its second block
+    tables[1, 3] = nb + 7    # sequence 1 its fourth (an id past the pool)
+    tables[2, :] = -1        # sequence 2 has no block at all
+    keep = [np.ones(L, bool) for _ in range(S)]
+    keep[0][B:2 * B] = False
+    keep[1][3 * B:4 * B] = False
+    keep[2][:] = False
+    return rng, Kd, Vd, kc, vc, tables, keep, L
+
+
+def test_decode_drops_keys_of_missing_blocks():
+    # The library skips a table entry outside the pool: those positions hold
+    # no key.  The oracle's result must equal SDPA over the dense K/V with
+    # the missing block's rows deleted (numpy indexing, not the table walk),
+    # and a sequence with no block left yields zeros.
+    rng, Kd, Vd, kc, vc, tables, keep, L = _missing_case()
+    Hq, D = 4, Kd.shape[-1]
+    q = rng.standard_normal((3, Hq, D))
+    scale = 0.3
+    lens = np.full(3, L, np.int32)
+    with pytest.raises(ValueError):
+        oracle.decode_attention(q, kc, vc, tables, lens, scale)
+    got = oracle.decode_attention(q, kc, vc, tables, lens, scale, drop_missing_blocks=True)
+    for s in (0, 1):
+        K = Kd[s][keep[s]].transpose(1, 0, 2).copy()
+        V = Vd[s][keep[s]].transpose(1, 0, 2).copy()
+        ref = _sdpa(q[s][:, None, :], K, V, scale)[:, 0, :]
+        np.testing.assert_allclose(got[s], ref, rtol=1e-12, atol=1e-12)
+    assert (got[2] == 0).all()
+
+
+def test_prefill_drops_keys_of_missing_blocks_and_keeps_positions():
+    # A 12-token chunk at the end of each 40-token sequence; keys of missing
+    # blocks are gone but the rest keep their absolute positions, so the
+    # causal mask is built from positions (explicit SDPA mask).
+    rng, Kd, Vd, kc, vc, tables, keep, L = _missing_case()
+    Hq, D, q_len = 4, Kd.shape[-1], 12
+    ctx = L - q_len
+    cu = np.arange(4, dtype=np.int32) * q_len
+    q = rng.standard_normal((3 * q_len, Hq, D))
+    scale = 0.25
+    lens = np.full(3, L, np.int32)
+    got = oracle.prefill_attention(q, cu, kc, vc, tables, lens, scale, drop_missing_blocks=True)
+    for s in (0, 1):
+        pos = np.flatnonzero(keep[s])
+        K = Kd[s][pos].transpose(1, 0, 2).copy()
+        V = Vd[s][pos].transpose(1, 0, 2).copy()
+        mask = torch.from_numpy(pos[None, :] <= (ctx + np.arange(q_len))[:, None])
+        qs = q[s * q_len:(s + 1) * q_len].transpose(1, 0, 2).copy()
+        ref = _sdpa(qs, K, V, scale, attn_mask=mask).transpose(1, 0, 2)
+        np.testing.assert_allclose(got[s * q_len:(s + 1) * q_len], ref, rtol=1e-12, atol=1e-12)
+    assert (got[2 * q_len:] == 0).all()
+
+
+def test_prefill_row_before_any_present_key_is_zero():
+    # Sequence 0's first block missing and a chunk starting at position 0:
+    # rows 0 .. B-1 see only missing positions and yield zeros; row B sees
+    # exactly one key, so its output is that key's value row.
+    B, Hq, Hkv, D = 8, 2, 1, 8
+    rng = np.random.default_rng(5)
+    Kd = rng.standard_normal((1, 2 * B, Hkv, D))
+    Vd = rng.standard_normal((1, 2 * B, Hkv, D))
+    kc, vc, tables = _identity_pool(Kd, Vd, B)
+    tables = tables.copy()
+    tables[0, 0] = -5
+    q = rng.standard_normal((2 * B, Hq, D))
+    got = oracle.prefill_attention(q, np.array([0, 2 * B], np.int32), kc, vc, tables, np.array([2 * B], np.int32),
+                                   0.5, drop_missing_blocks=True)
+    assert (got[:B] == 0).all()
+    for h in range(Hq):
+        np.testing.assert_array_equal(got[B, h], Vd[0, B, 0])

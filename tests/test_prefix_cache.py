@@ -207,3 +207,34 @@ def test_manager_prefix_errors(pa):
         bm.set_hash_bits(0)
     assert e.value.status == 2
     bm.close()
+
+
+def test_model_whole_block_prompt_keeps_its_last_block_private():
+    # A 64-token prompt (exactly 4 blocks) fully cached: reusing all four
+    # would leave no token to compute, and recomputing the last position
+    # would write into a shared cached block.  Only the first three are
+    # reused; the fourth is a fresh private block.
+    m = oracle.BlockPoolModel(16, B)
+    m.add_sequence_tokens(0, PROMPT)
+    m.commit(0, 64)
+    assert m.add_sequence_tokens(1, PROMPT) == 48
+    assert m.tables[1][:3] == m.tables[0][:3]
+    assert m.tables[1][3] != m.tables[0][3] and m.refs[m.tables[1][3]] == 1
+    # One more token: all four full blocks are shared again.
+    assert m.add_sequence_tokens(2, PROMPT + [5]) == 64
+    assert m.add_sequence_tokens(3, PROMPT[:16]) == 0  # a one-block prompt reuses nothing
+    assert m.add_sequence_tokens(4, []) == 0
+
+
+def test_manager_whole_block_prompt_keeps_its_last_block_private(pa):
+    bm = pa.BlockManager(16, B)
+    model = oracle.BlockPoolModel(16, B)
+    for sid, toks in ((0, PROMPT), (1, PROMPT), (2, PROMPT + [5]), (3, PROMPT[:16])):
+        want = model.add_sequence_tokens(sid, toks)
+        assert bm.add_sequence_tokens(sid, toks) == want
+        if sid == 0:
+            model.commit(0, 64)
+            bm.commit(0, 64)
+        assert bm.block_table(sid) == model.tables[sid]
+    assert bm.add_sequence_tokens(1 + 10, PROMPT) == 48
+    bm.close()

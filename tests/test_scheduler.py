@@ -204,3 +204,72 @@ def test_scheduler_errors(pa):
         bm.block_table(1)  # released
     sc.close()
     bm.close()
+
+
+def test_forked_request_surfaces_its_copy_on_write_pair(pa):
+    # Request A (20-token prompt: its second block holds 4 tokens) is forked
+    # through the block manager (parallel sampling).  When A's next token is
+    # scheduled, its shared, partly filled last block must be replaced by a
+    # private copy, and the scheduler must report the (old, new) pair: the
+    # caller copies the block before writing the token, else the token's
+    # earlier neighbours in that block would be garbage.
+    order = np.arange(8)[::-1].copy()
+    bm = pa.BlockManager(8, 16, order)
+    sc = pa.Scheduler(bm, 4)
+    m = _model(8, 16, 4, order)
+    for x in (sc, m):
+        x.add_request("A" if x is m else 1, 20, 4)
+    assert m.schedule() == ["A"] and sc.schedule() == [1]
+    assert sc.copies() == [] and m.copies == []
+    m.pool.fork("A", "child")
+    bm.fork(1, 99)
+    old = bm.block_table(1)[1]
+    assert bm.refcount(old) == 2
+    m.step("A")
+    sc.step(1)
+    assert m.schedule() == ["A"] and sc.schedule() == [1]
+    new = bm.block_table(1)[1]
+    assert new != old and bm.block_table(99)[1] == old
+    assert sc.copies() == [(old, new)] == m.copies
+    assert bm.refcount(old) == 1 and bm.refcount(new) == 1
+    # The next iteration appends into the now private block: no pair.
+    m.step("A")
+    sc.step(1)
+    m.schedule()
+    sc.schedule()
+    assert sc.copies() == [] == m.copies
+    sc.close()
+    bm.close()
+
+
+def test_scheduler_copies_match_model_with_random_forks(pa):
+    rng = np.random.default_rng(77)
+    for trial in range(15):
+        nb, B, mb = int(rng.integers(8, 40)), int(rng.choice([4, 16])), int(rng.integers(1, 6))
+        order = rng.permutation(nb)
+        bm = pa.BlockManager(nb, B, order)
+        sc = pa.Scheduler(bm, mb)
+        m = _model(nb, B, mb, order)
+        nxt, child = 0, 10_000
+        for _ in range(60):
+            if rng.random() < 0.5:
+                p, mt = int(rng.integers(1, 3 * B)), int(rng.integers(1, 2 * B))
+                m.add_request(nxt, p, mt)
+                sc.add_request(nxt, p, mt)
+                nxt += 1
+            want = m.schedule()
+            assert sc.schedule() == want
+            assert sc.copies() == m.copies
+            assert bm.free_list() == list(m.pool.free)
+            if want and rng.random() < 0.3:  # fork one scheduled request
+                rid = int(rng.choice(want))
+                if m.state(rid) == oracle.scheduler.DECODING:
+                    m.pool.fork(rid, child)
+                    bm.fork(rid, child)
+                    child += 1
+            for rid in want:
+                if m.state(rid) == oracle.scheduler.DECODING and rng.random() < 0.9:
+                    m.step(rid)
+                    sc.step(rid)
+        sc.close()
+        bm.close()
