@@ -287,6 +287,25 @@ typedef struct {
 
 pa_status pa_decode_run(const pa_decode_args* args, hipStream_t stream);
 
+/* pa_decode_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument.  The per-partition partials live in a fixed
+ * library-owned scratch array of PA_NOALLOC_SCRATCH_BYTES in each GPU's
+ * memory (held until the process ends); the call allocates nothing.  A
+ * batch whose partials need more than that (pa_decode_workspace_bytes with
+ * the same arguments) is refused with PA_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ * time on one GPU (different streams, or other threads) race and must be
+ * serialised by the caller; calls on one stream are ordered.  The scratch
+ * needs no clearing: every partition writes its partials (or an absent
+ * marker) before the merge reads them. */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status pa_decode_noalloc(const pa_kv_cache* cache, void* out, const void* query,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t max_seq_len, float scale, int32_t partition_size,
+                            hipStream_t stream);
+
 /* Host-side work list for decode batches of mixed lengths (no device
  * memory; the caller's scheduler knows the lengths).  Lists, for the host
  * copy of seq_lens (clamped to [0, max_seq_len]), every partition that

@@ -3,6 +3,7 @@
 // launch; a failed check launches nothing.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -66,6 +67,36 @@ WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int num_partitions
   w.o_off = w.l_off + align256(rows * 4);
   w.bytes = w.o_off + align256(rows * head_dim * 4);
   return w;
+}
+
+// Decode partials of pa_decode_noalloc: one fixed array per GPU, held until
+// the process ends.  Host code never passes this name to a kernel (on the
+// host it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up once per device),
+// or nullptr if the runtime cannot give it.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -307,6 +338,26 @@ int32_t pa_decode_plan(const int32_t* seq_lens_host, int32_t num_seqs, int32_t m
   if (work && capacity >= n)
     for (int32_t k = 0; k < n; ++k) work[k] = (int32_t)(units[k].s * np + units[k].part);
   return n;
+}
+
+pa_status pa_decode_noalloc(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t max_seq_len, float scale, int32_t partition_size, hipStream_t stream) {
+  const pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || num_heads <= 0) return PA_ERR_SHAPE;
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads, cache->head_dim,
+                                                cache->block_size, max_seq_len, partition_size);
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  pa_decode_args d = basic_args(cache, out, query, block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_heads,
+                                max_seq_len, scale, nullptr, 0, partition_size);
+  if (need > 0 && num_seqs > 0) {
+    void* ws = scratch_on_current_device();
+    if (!ws) return PA_ERR_LAUNCH;
+    d.workspace = ws;
+    d.workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
+  return decode_run(&d, stream);
 }
 
 pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,

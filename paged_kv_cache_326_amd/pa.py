@@ -93,6 +93,7 @@ EXPORTS = (
     "pa_decode_append",
     "pa_decode_run",
     "pa_decode_plan",
+    "pa_decode_noalloc",
     "pa_prefill_chunk",
     "pa_copy_blocks",
     "pa_gather_blocks",
@@ -157,6 +158,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_ex.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp]
     L.pa_decode_ex.restype = ctypes.c_int
+    L.pa_decode_noalloc.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, i32, vp]
+    L.pa_decode_noalloc.restype = ctypes.c_int
     L.pa_decode_stage.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, i32, vp]
     L.pa_decode_stage.restype = ctypes.c_int
     L.pa_decode_timed.argtypes = [cache_p, vp, vp, i32p, i32, i32p, i32, i32, i32, f32, vp, sz, i32, vp, vp, vp]
@@ -388,6 +391,31 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale:
     else:
         st = lib().pa_decode_ex(*args, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+# Scratch bytes pa_decode_noalloc has on each GPU (PA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                      partition_size: int = 0, stream=None, scales=None):
+    """Decode attention with the library's fixed per-GPU scratch instead of a
+    workspace (pa_decode_noalloc): nothing is allocated, here or in the
+    library.  Calls that overlap in time on one GPU share that scratch and
+    race."""
+    c = kv_cache(key_cache, value_cache, scales)
+    _need(query, "query", io_dtype(key_cache))
+    _need(out, "out", io_dtype(key_cache))
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = query.shape
+    if out.shape != query.shape or D != c.head_dim or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("shape mismatch between query/out/block_tables/seq_lens and the cache")
+    st = lib().pa_decode_noalloc(ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(),
+                                 block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
+                                 int(partition_size), _stream(stream))
+    _check(st, "pa_decode_noalloc")
     return out
 
 
