@@ -17,12 +17,14 @@
  * KV pool ([P1] "KV Cache 的内存开销与分页机制", fixed-size physical blocks;
  * [P2] section 2.1, one pool preallocated up front).  One layer's pool is two
  * arrays
- *     key_cache   : [num_blocks][num_kv_heads][block_size][head_dim]
+ *     key_cache   : [num_blocks][num_kv_heads][head_dim / kc][block_size][kc]
  *     value_cache : [num_blocks][num_kv_heads][head_dim][block_size]
- * so that the block_size token vectors of one (block, KV head) are one
- * contiguous tile ([P1] "PagedAttention 的 CUDA Kernel 实现": vectors of a
- * block sit together so that reads coalesce); value tiles are stored
- * transposed (see pa_kv_cache).  A slot numbers token positions in the pool:
+ * (kc = 64 bytes of elements: 16 float32, 32 float16 / bfloat16, 64 FP8
+ * codes) so that the block_size token vectors of one (block, KV head) are
+ * one contiguous tile ([P1] "PagedAttention 的 CUDA Kernel 实现": vectors of
+ * a block sit together so that reads coalesce); inside a tile the key rows
+ * are cut into 64-byte column chunks and the value tile is transposed (see
+ * pa_kv_cache).  A slot numbers token positions in the pool:
  * slot = physical_block * block_size + offset.
  *
  * Block tables ([P1] "KV Cache 的内存开销与分页机制": one table per request,
@@ -84,12 +86,16 @@ typedef enum {
 } pa_status;
 
 /* One layer's paged KV pool.  Both arrays are device memory owned by the
- * caller, in `dtype`: key_cache [num_blocks][num_kv_heads][block_size][head_dim]
- * and value_cache [num_blocks][num_kv_heads][head_dim][block_size].  Every
- * (block, KV head) tile is contiguous ([P1] "PagedAttention 的 CUDA Kernel
- * 实现": a block's vectors are adjacent so its reads coalesce); value tiles
- * are stored transposed so that the tokens of one dimension are adjacent,
- * which makes both attention products contiguous matrix-core operand loads.
+ * caller, in `dtype`: key_cache [num_blocks][num_kv_heads][head_dim / kc]
+ * [block_size][kc] with kc = 64 / (bytes per element), and value_cache
+ * [num_blocks][num_kv_heads][head_dim][block_size].  Every (block, KV head)
+ * tile is contiguous ([P1] "PagedAttention 的 CUDA Kernel 实现": a block's
+ * vectors are adjacent so its reads coalesce).  Inside a key tile, key
+ * element (offset t, dim d) sits at (d / kc) * block_size * kc + t * kc +
+ * d % kc: the rows are cut into 64-byte column chunks, so a matrix-core
+ * operand (64 bytes of each of 16 rows) is whole 128-byte lines.  Value
+ * tiles are stored transposed so that the tokens of one dimension are
+ * adjacent, which makes the PV product's operand a contiguous load.
  * k_scale and v_scale are read only for PA_FP8_E4M3 (must then be positive
  * and finite, else PA_ERR_SHAPE): a key code c stands for value(c) * k_scale,
  * a value code for value(c) * v_scale.  New rows are quantised as
@@ -360,7 +366,8 @@ pa_status pa_prefill_chunk(const pa_kv_cache* cache, void* out, const void* quer
  * pa_gather_blocks   pool block block_ids[i] -> row i of key_out/value_out
  * pa_scatter_blocks  row i of key_in/value_in -> pool block block_ids[i]
  * Buffers are laid out like the pool's blocks (key: [n][num_kv_heads]
- * [block_size][head_dim], value: [n][num_kv_heads][head_dim][block_size]) in
+ * [head_dim / kc][block_size][kc], value: [n][num_kv_heads][head_dim]
+ * [block_size]) in
  * the cache dtype, device memory or pinned host memory (hipHostMalloc), so a gather or
  * scatter through a pinned buffer swaps blocks out of or into HBM; other
  * host memory is refused with PA_ERR_UNSUPPORTED.  Ids outside

@@ -67,6 +67,8 @@ from .paging import (  # noqa: F401
     slot_mapping,
     reshape_and_cache,
     gather_kv,
+    key_rows,
+    key_tiles,
 )
 from .attention import decode_attention, prefill_attention  # noqa: F401
 from .block_pool import BlockPoolModel, NoBlocks, copy_blocks, gather_blocks, scatter_blocks  # noqa: F401

@@ -86,6 +86,37 @@ def slot_mapping(
     return np.asarray(out, dtype=np.int64)
 
 
+# Pool layouts.  Each (block, KV head) tile is one contiguous piece of memory,
+# the property that lets in-block KV reads coalesce ([P1] "PagedAttention 的
+# CUDA Kernel 实现").  Values: [num_blocks, num_kv_heads, head_dim,
+# block_size] (a dimension's block_size values adjacent).  Keys:
+# [num_blocks, num_kv_heads, head_dim // kc, block_size, kc]: the tile's
+# block_size rows cut into column chunks of kc dims (64 bytes of the storage
+# type: 16 float32, 32 float16/bfloat16, 64 FP8 codes), chunk after chunk,
+# each chunk row after row.  Key element (block b, head h, offset t, dim d)
+# is key_cache[b, h, d // kc, t, d % kc].
+
+
+def key_rows(key_cache: np.ndarray) -> np.ndarray:
+    """Key tiles [NB, H, head_dim // kc, B, kc] -> rows [NB, H, B, head_dim]."""
+    NB, H, NC, B, KC = key_cache.shape
+    out = np.empty((NB, H, B, NC * KC), dtype=key_cache.dtype)
+    for q in range(NC):
+        out[:, :, :, q * KC:(q + 1) * KC] = key_cache[:, :, q, :, :]
+    return out
+
+
+def key_tiles(rows: np.ndarray, kc: int) -> np.ndarray:
+    """Rows [NB, H, B, head_dim] -> key tiles [NB, H, head_dim // kc, B, kc]."""
+    NB, H, B, D = rows.shape
+    if D % kc:
+        raise ValueError("head_dim must be a multiple of the key chunk")
+    out = np.empty((NB, H, D // kc, B, kc), dtype=rows.dtype)
+    for q in range(D // kc):
+        out[:, :, q, :, :] = rows[:, :, :, q * kc:(q + 1) * kc]
+    return out
+
+
 def reshape_and_cache(
     key_cache: np.ndarray,
     value_cache: np.ndarray,
@@ -95,15 +126,12 @@ def reshape_and_cache(
 ) -> None:
     """Write each new token's K and V (all KV heads) into its pool slot, in place.
 
-    Pool layouts: keys [num_blocks, num_kv_heads, block_size, head_dim],
-    values [num_blocks, num_kv_heads, head_dim, block_size].  Each (block, KV
-    head) tile is one contiguous piece of memory, the property that lets
-    in-block KV reads coalesce ([P1] "PagedAttention 的 CUDA Kernel 实现");
-    inside a value tile a dimension's block_size values are adjacent.
-    A negative slot marks a padding token and is skipped; two tokens may not
-    share a slot.  Values are copied bit for bit.
+    Pool layouts as above: the key row lands as one kc-wide piece of every
+    chunk of its block's key tile, the value row as column `offset` of the
+    value tile.  A negative slot marks a padding token and is skipped; two
+    tokens may not share a slot.  Values are copied bit for bit.
     """
-    B = key_cache.shape[2]
+    NC, B, KC = key_cache.shape[2:]
     slots = np.asarray(slots, dtype=np.int64)
     valid = slots[slots >= 0]
     if len(np.unique(valid)) != len(valid):
@@ -112,7 +140,8 @@ def reshape_and_cache(
         if slot < 0:
             continue
         block, offset = int(slot) // B, int(slot) % B
-        key_cache[block, :, offset, :] = key[t]
+        for q in range(NC):
+            key_cache[block, :, q, offset, :] = key[t][:, q * KC:(q + 1) * KC]
         value_cache[block, :, :, offset] = value[t]
 
 
@@ -126,15 +155,15 @@ def gather_kv_present(key_cache: np.ndarray, value_cache: np.ndarray, table_row:
     tokens keep their positions (and so their causal visibility).  Built
     token by token from the definition of the table walk.
     """
-    B, nb = key_cache.shape[2], key_cache.shape[0]
+    nb, Hkv, NC, B, KC = key_cache.shape
     ks, vs, pos = [], [], []
     for t in range(seq_len):
         phys = int(table_row[t // B])
         if 0 <= phys < nb:
-            ks.append(key_cache[phys, :, t % B, :])
+            ks.append(np.concatenate([key_cache[phys, :, q, t % B, :] for q in range(NC)], axis=1))
             vs.append(value_cache[phys, :, :, t % B])
             pos.append(t)
-    Hkv, D = key_cache.shape[1], key_cache.shape[3]
+    D = NC * KC
     if not pos:
         return np.zeros((0, Hkv, D)), np.zeros((0, Hkv, D)), np.zeros(0, dtype=np.int64)
     return np.stack(ks), np.stack(vs), np.asarray(pos, dtype=np.int64)
@@ -148,13 +177,14 @@ def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, table_row: np.ndar
     Only the first ``blocks_needed(seq_len)`` table entries are read, and of
     the last block only the filled offsets.
     """
-    B = key_cache.shape[2]
+    B = key_cache.shape[3]
     n = blocks_needed(seq_len, B)
     phys = np.asarray(table_row[:n], dtype=np.int64)
     if ((phys < 0) | (phys >= key_cache.shape[0])).any():
         raise ValueError("a table entry names a block outside the pool")
     # Logical order is block-major, offset-minor:
-    # keys [n, Hkv, B, D] -> [n, B, Hkv, D]; values [n, Hkv, D, B] -> [n, B, Hkv, D].
-    K = key_cache[phys].transpose(0, 2, 1, 3).reshape(n * B, key_cache.shape[1], key_cache.shape[3])
+    # keys -> rows [n, Hkv, B, D] -> [n, B, Hkv, D]; values [n, Hkv, D, B] -> [n, B, Hkv, D].
+    rows = key_rows(key_cache[phys])
+    K = rows.transpose(0, 2, 1, 3).reshape(n * B, rows.shape[1], rows.shape[3])
     V = value_cache[phys].transpose(0, 3, 1, 2).reshape(n * B, value_cache.shape[1], value_cache.shape[2])
     return K[:seq_len], V[:seq_len]

@@ -36,11 +36,10 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(
 
 // The scatter works on groups of up to kGroup consecutive entries of the
 // token list; one workgroup per group.  A token row of one KV head is
-// head_dim elements.  The key tile of (block, KV head) is
-// [block_size][head_dim] (the row lands at
-//   ((block * num_kv_heads + head) * block_size + offset) * head_dim),
-// the value tile [head_dim][block_size] (the row becomes column `offset`).
-// Key rows move as 16-byte chunks.  Value rows: when the group's kGroup
+// head_dim elements.  The key tile of (block, KV head) holds block_size rows
+// in 64-byte column chunks (row `offset` becomes one 64-byte piece of every
+// chunk), the value tile is [head_dim][block_size] (the row becomes column
+// `offset`).  Key rows move as 16-byte chunks.  Value rows: when the group's kGroup
 // slots are consecutive and the first is a multiple of kGroup (so they lie
 // in one block, block_size being a multiple of kGroup; the usual case for a
 // prefill chunk), each thread loads one 16-byte chunk (VEC dims) of all

@@ -229,6 +229,8 @@ decode_partition_kernel(DecodeArgs a) {
   constexpr int CE = Dec<T>::CE, KE = Dec<T>::KE, VW = Dec<T>::VW;
   constexpr int NBUF = WaveCfg<kNW, T>::kRing;
   constexpr int NLK = D / (4 * CE);                 // K loads per lane per 16-token half
+  constexpr int KC = key_chunk<T>();                // elements per 64-byte key chunk (= 4 * CE)
+  static_assert(KC == 4 * CE, "one key load instruction covers one 64-byte chunk of 16 rows");
   constexpr int NSUB = CE / KE;                     // products per K load
   constexpr int QW = CE * (int)sizeof(QT) / 16;     // 16-byte query pieces per K load
   constexpr int NDT = D / 16;                       // 16-dim tiles of the PV product
@@ -357,15 +359,14 @@ decode_partition_kernel(DecodeArgs a) {
       const int t = stok + 8 * (r >> 2) + 4 * c + (r & 3);
       const int j = t / B;
       const int pb = (t < ntok && j < nbp) ? s_bt[j] : -1;
-      const T* src = kbase + (int64_t)pb * blk_stride + (t % B) * D + CE * grp;
-      // Ordinary loads for K: each instruction reads 64 bytes of 16 key
-      // rows and the next one the other half of the same 128-byte lines,
-      // which the caches then still hold (and a block shared by several
-      // sequences is found there too).  V, read once in whole lines, is
-      // streamed with non-temporal loads.
+      // Key load ls reads 64-byte chunk ls of the 16 rows: rows 8(r/4) +
+      // 4c .. +3 are adjacent in a chunk, so the wave reads whole 128-byte
+      // lines, each once; K and V are streamed with non-temporal loads.
+      const T* src = kbase + (int64_t)pb * blk_stride + (t % B) * KC + CE * grp;
 #pragma unroll
       for (int ls = 0; ls < NLK; ++ls)
-        b.k[c][ls] = pb >= 0 ? *reinterpret_cast<const u32x4*>(src + 4 * CE * ls) : u32x4{0, 0, 0, 0};
+        b.k[c][ls] = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)ls * B * KC))
+                             : u32x4{0, 0, 0, 0};
     }
     const int t0 = stok + 8 * grp;
     const int j = t0 / B;

@@ -177,14 +177,34 @@ __device__ __forceinline__ void store_column(T* p, int64_t stride, const u32x4 d
   }
 }
 
+// Key tiles.  The key tile of one (block, KV head), block_size rows of
+// head_dim elements, is stored as 64-byte column chunks: chunk q holds dims
+// q*KC .. q*KC+KC-1 (KC = 64 bytes of elements) of every row, row after row,
+// so element (row t, dim d) sits at (d / KC) * block_size * KC + t * KC +
+// d % KC of the tile.  A wave that reads a 64-byte piece of each of 16 rows
+// (one matrix-core operand) then reads whole 128-byte lines.
+template <typename T>
+constexpr int key_chunk() {
+  return 64 / Elem<T>::kBytes;
+}
+
+// Offset (elements) of (row t, dim d) inside a key tile.
+template <typename T>
+__host__ __device__ __forceinline__ int64_t key_tile_offset(int t, int d, int block_size) {
+  constexpr int KC = key_chunk<T>();
+  return (int64_t)(d / KC) * block_size * KC + (int64_t)t * KC + d % KC;
+}
+
 // The destination of one 16-byte source chunk (dims ch*VEC ..) of token
-// slot (blk, off), KV head h: a key row piece, or a value column piece.
+// slot (blk, off), KV head h: a key row piece (inside one 64-byte key
+// chunk, VEC dividing it), or a value column piece.
 template <typename T>
 __device__ __forceinline__ void store_kv_chunk(T* key_cache, T* value_cache, int which, int64_t blk, int off, int h,
                                                int ch, int vec, int num_kv_heads, int head_dim, int block_size,
                                                const u32x4 data, float k_scale, float v_scale) {
   if (which == 0) {
-    T* dst = key_cache + ((blk * num_kv_heads + h) * block_size + off) * head_dim + ch * vec;
+    T* dst = key_cache + (blk * num_kv_heads + h) * (int64_t)block_size * head_dim +
+             key_tile_offset<T>(off, ch * vec, block_size);
     store_chunk<T>(dst, data, k_scale);
   } else {
     T* dst = value_cache + ((blk * num_kv_heads + h) * head_dim + ch * vec) * block_size + off;

@@ -207,7 +207,16 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
     return (id >= 0 && id < a.cache.num_blocks) ? id : -1;
   };
 
-  // Global -> registers for one tile.  K chunks: key-major (coalesced rows);
+  // K piece c of a tile: 16 bytes (dims dch*CE ..) of key `key`, numbered
+  // in the pool's order (the four pieces of a key's 64-byte chunk, then the
+  // tile's keys, then the chunks), so consecutive threads read consecutive
+  // memory.
+  constexpr int KPC = key_chunk<T>() / CE;  // 16-byte pieces per 64-byte chunk
+  auto key_piece = [&](int c, int& key, int& dch) {
+    key = (c / KPC) % kKT;
+    dch = (c / (KPC * kKT)) * KPC + c % KPC;
+  };
+  // Global -> registers for one tile.  K chunks in pool order (coalesced);
   // V chunks: CE keys of one dimension from the transposed value tile (a
   // tile of 32 keys never splits such a piece across blocks, since CE
   // divides the block size).  Keys no row of this workgroup sees (>= kend),
@@ -221,13 +230,15 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       const int c = tid + i * NT;
       if (NCHK % NT != 0 && c >= NCHK) continue;
       {
-        const int key = c / (D / CE), dch = c % (D / CE);
+        int key, dch;
+        key_piece(c, key, dch);
         const int pos = t * kKT + key;
         u32x4 x = {0, 0, 0, 0};
         if (pos < kend) {  // keys >= kend are masked for every row of this tile
           const int pb = block_of(pos);
           if (pb >= 0)
-            x = *reinterpret_cast<const u32x4*>(kc + (((int64_t)pb * Hkv + g) * B + pos % B) * D + dch * CE);
+            x = *reinterpret_cast<const u32x4*>(kc + ((int64_t)pb * Hkv + g) * B * D +
+                                                key_tile_offset<T>(pos % B, dch * CE, B));
         }
         kreg[i] = x;
       }
@@ -284,7 +295,8 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
       const int c = tid + i * NT;
       if (NCHK % NT != 0 && c >= NCHK) continue;
       {
-        const int key = c / (D / CE), dch = c % (D / CE);
+        int key, dch;
+        key_piece(c, key, dch);
         put(Ks(st) + key * S::kKStride + dch * CE, kreg[i]);
       }
       {

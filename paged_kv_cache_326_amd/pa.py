@@ -261,10 +261,20 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def key_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype: torch.dtype):
+    """Shape of a key pool: each (block, KV head) tile's block_size rows cut
+    into column chunks of 64 bytes of elements,
+    [num_blocks, num_kv_heads, head_dim // kc, block_size, kc]."""
+    kc = 64 // torch.empty((), dtype=dtype).element_size()
+    if head_dim % kc:
+        raise ValueError(f"head_dim {head_dim} is not a multiple of the {kc}-element key chunk")
+    return (num_blocks, num_kv_heads, head_dim // kc, block_size, kc)
+
+
 def value_shape(key_shape):
     """Shape of the value pool that goes with a key pool of ``key_shape``."""
-    NB, H, B, D = key_shape
-    return (NB, H, D, B)
+    NB, H, NC, B, KC = key_shape
+    return (NB, H, NC * KC, B)
 
 
 def is_fp8(key_cache: torch.Tensor) -> bool:
@@ -277,7 +287,8 @@ def io_dtype(key_cache: torch.Tensor) -> torch.dtype:
 
 
 def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor, scales=None) -> pa_kv_cache:
-    """Describe a pool: keys [num_blocks, num_kv_heads, block_size, head_dim],
+    """Describe a pool: keys [num_blocks, num_kv_heads, head_dim // kc,
+    block_size, kc] (key_shape: 64-byte column chunks of each key tile),
     values [num_blocks, num_kv_heads, head_dim, block_size] (each value tile
     transposed).
 
@@ -285,16 +296,20 @@ def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor, scales=None) ->
     stands for value(c) * scale."""
     _need(key_cache, "key_cache")
     _need(value_cache, "value_cache", key_cache.dtype)
-    if key_cache.dim() != 4 or value_cache.dim() != 4 or value_cache.shape != value_shape(key_cache.shape):
-        raise ValueError("key_cache must be [num_blocks, num_kv_heads, block_size, head_dim] and value_cache "
-                         "[num_blocks, num_kv_heads, head_dim, block_size]")
     if key_cache.dtype not in _DTYPE:
         raise ValueError(f"unsupported cache dtype {key_cache.dtype}")
+    ok = key_cache.dim() == 5 and value_cache.dim() == 4
+    if ok:
+        NB, H, NC, B, KC = key_cache.shape
+        ok = key_cache.shape == key_shape(NB, H, B, NC * KC, key_cache.dtype) and \
+            value_cache.shape == value_shape(key_cache.shape)
+    if not ok:
+        raise ValueError("key_cache must be [num_blocks, num_kv_heads, head_dim // kc, block_size, kc] with kc = 64 "
+                         "bytes of elements, and value_cache [num_blocks, num_kv_heads, head_dim, block_size]")
     if is_fp8(key_cache) and scales is None:
         raise ValueError("an FP8 pool needs scales=(k_scale, v_scale)")
     ks, vs = (1.0, 1.0) if scales is None else (float(scales[0]), float(scales[1]))
-    NB, H, B, D = key_cache.shape
-    return pa_kv_cache(key_cache.data_ptr(), value_cache.data_ptr(), NB, H, D, B, _DTYPE[key_cache.dtype], ks, vs)
+    return pa_kv_cache(key_cache.data_ptr(), value_cache.data_ptr(), NB, H, NC * KC, B, _DTYPE[key_cache.dtype], ks, vs)
 
 
 def _check(status: int, what: str):
@@ -363,7 +378,7 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block
 def decode_workspace(query, key_cache, max_seq_len: int, partition_size: int = 0) -> torch.Tensor:
     """Allocate (with torch) the scratch pa_decode needs for these shapes."""
     S, Hq, D = query.shape
-    n = pa_decode_workspace_bytes(S, Hq, key_cache.shape[1], D, key_cache.shape[2], max_seq_len, partition_size)
+    n = pa_decode_workspace_bytes(S, Hq, key_cache.shape[1], D, key_cache.shape[3], max_seq_len, partition_size)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=query.device)
 
 

@@ -12,7 +12,10 @@ Sources (web pages on paged KV caches):
 
 Layout (one layer's pool, [P1] "KV Cache 的内存开销与分页机制": fixed-size
 physical blocks, a per-request block table):
-  key_cache              : [num_blocks, num_kv_heads, block_size, head_dim]
+  key_cache              : [num_blocks, num_kv_heads, head_dim // kc,
+                            block_size, kc]: each key tile's rows cut into
+                           column chunks of kc = 64 bytes of elements
+                           (16 float32, 32 float16 / bfloat16)
   value_cache            : [num_blocks, num_kv_heads, head_dim, block_size]
                            (each value tile transposed)
   block_tables           : int32 [num_seqs, max_blocks_per_seq]
@@ -42,6 +45,18 @@ import numpy as np
 
 DTYPES = ("f32", "f16", "bf16")
 BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def key_chunk(elem_bytes: int) -> int:
+    """Elements per 64-byte column chunk of a key tile."""
+    return 64 // int(elem_bytes)
+
+
+def key_chunks_of(rows: np.ndarray, elem_bytes: int) -> np.ndarray:
+    """Key rows [NB, H, B, D] laid out as key tiles [NB, H, D // kc, B, kc]."""
+    NB, H, B, D = rows.shape
+    kc = key_chunk(elem_bytes)
+    return np.ascontiguousarray(rows.reshape(NB, H, B, D // kc, kc).transpose(0, 1, 3, 2, 4))
 
 
 def f32_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -84,7 +99,7 @@ class Workload:
     seq_lens: np.ndarray  # int32 [S]
     q_lens: np.ndarray  # int32 [S]
     block_tables: np.ndarray  # int32 [S, MB]
-    key_cache: np.ndarray  # storage [NB, Hkv, B, D], new-token slots not yet written
+    key_cache: np.ndarray  # storage [NB, Hkv, D // kc, B, kc], new-token slots not yet written
     value_cache: np.ndarray
     new_key: np.ndarray  # storage [T, Hkv, D]
     new_value: np.ndarray
@@ -238,7 +253,11 @@ def build(
 
     Hkv, D, Hq = num_kv_heads, head_dim, num_heads
     shape = (NB, Hkv, B, D)
-    kc = f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
+    if D % key_chunk(BYTES[dtype]):
+        raise ValueError("head_dim must be a multiple of the 64-byte key chunk")
+    # Keys are drawn in (block, head, token, dim) order and stored as key
+    # tiles of 64-byte column chunks.
+    kc = key_chunks_of(f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype), BYTES[dtype])
     # Values are drawn in the same (block, head, token, dim) order as keys
     # and stored with each tile transposed: [NB, Hkv, D, B].
     vc = np.ascontiguousarray(f32_to_storage(rng.standard_normal(shape, dtype=np.float32), dtype).transpose(0, 1, 3, 2))
@@ -259,7 +278,7 @@ def build(
                 live[tables[s, j], :n] = True
         dead = ~live
         nanv = nan_value(dtype)
-        kc.transpose(0, 2, 1, 3)[dead] = nanv
+        kc.transpose(0, 3, 1, 2, 4)[dead] = nanv
         vc.transpose(0, 3, 1, 2)[dead] = nanv
 
     return Workload(

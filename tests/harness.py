@@ -205,10 +205,12 @@ def fp8_pool_gpu(gw: GpuWorkload, scales):
     import torch
     from paged_kv_cache_326_amd import pa
 
-    NB, H, B, D = gw.key_cache.shape
-    kc8 = torch.zeros((NB, H, B, D), dtype=torch.uint8, device=gw.key_cache.device)
+    NB, H, NC, B, KC = gw.key_cache.shape
+    D = NC * KC
+    kc8 = torch.zeros(pa.key_shape(NB, H, B, D, torch.uint8), dtype=torch.uint8, device=gw.key_cache.device)
     vc8 = torch.zeros((NB, H, D, B), dtype=torch.uint8, device=gw.key_cache.device)
-    rows_k = gw.key_cache.permute(0, 2, 1, 3).reshape(NB * B, H, D).contiguous()
+    # Token rows of the key tiles: [NB, H, NC, B, KC] -> [NB, B, H, NC, KC].
+    rows_k = gw.key_cache.permute(0, 3, 1, 2, 4).reshape(NB * B, H, D).contiguous()
     rows_v = gw.value_cache.permute(0, 3, 1, 2).reshape(NB * B, H, D).contiguous()
     slots = torch.arange(NB * B, dtype=torch.int64, device=gw.key_cache.device)
     pa.pa_reshape_and_cache(kc8, vc8, rows_k, rows_v, slots, scales=scales)
@@ -219,7 +221,8 @@ def fp8_pool_oracle(w: synth.Workload, scales):
     """The oracle's codes for the same pool."""
     import oracle
 
-    return oracle.fp8_quantize(w.key_cache, scales[0]), oracle.fp8_quantize(w.value_cache, scales[1])
+    keys = oracle.key_tiles(oracle.fp8_quantize(oracle.key_rows(w.key_cache), scales[0]), 64)
+    return keys, oracle.fp8_quantize(w.value_cache, scales[1])
 
 
 def ramped_keys(w, slope, seed):
@@ -240,7 +243,9 @@ def ramped_keys(w, slope, seed):
             row = (0.5 + slope * j) * u + 0.01 * rng.standard_normal((w.num_kv_heads, D))
             row = synth.f32_to_storage(row.astype(np.float32), w.dtype)
             if j < L - q:
-                kc[w.block_tables[s, j // B], :, j % B, :] = row
+                KC = kc.shape[4]
+                for ch in range(kc.shape[2]):
+                    kc[w.block_tables[s, j // B], :, ch, j % B, :] = row[:, ch * KC:(ch + 1) * KC]
             else:
                 nk[cu[s] + j - (L - q)] = row
     qry = synth.f32_to_storage(np.broadcast_to(u, w.query.shape).astype(np.float32), w.dtype)

@@ -93,7 +93,7 @@ def test_copy_on_write_fork_decodes_like_the_oracle():
     t0, t1 = bm.block_table(0), bm.block_table(1)
     assert t0[:2] == t1[:2] and t0[2] == old and t1[2] == fresh
 
-    kc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D), dtype=np.float32), dt)
+    kc = synth.key_chunks_of(synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D), dtype=np.float32), dt), 2)
     vc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, D, B), dtype=np.float32), dt)  # value tiles [D][B]
     nk = synth.f32_to_storage(rng.standard_normal((2, Hkv, D), dtype=np.float32), dt)
     nv = synth.f32_to_storage(rng.standard_normal((2, Hkv, D), dtype=np.float32), dt)
@@ -115,8 +115,8 @@ def test_copy_on_write_fork_decodes_like_the_oracle():
     oracle.copy_blocks(k64, [old], [fresh])
     oracle.copy_blocks(v64, [old], [fresh])
     for s, blk in enumerate((old, fresh)):
-        k64[blk, :, 37 % B] = oracle.to_float64(nk[s], dt)
-        v64[blk, :, :, 37 % B] = oracle.to_float64(nv[s], dt)
+        oracle.reshape_and_cache(k64, v64, oracle.to_float64(nk[s:s + 1], dt), oracle.to_float64(nv[s:s + 1], dt),
+                                 np.array([blk * B + 37 % B]))
     ref = oracle.decode_attention(oracle.to_float64(q, dt), k64, v64, tables, lens, 1 / np.sqrt(D))
     ok, maxerr, nbad = harness.tolerance_ok(oracle.to_float64(harness.from_device(out, dt), dt), ref, dt)
     assert ok, (maxerr, nbad)
@@ -149,7 +149,7 @@ def test_prefix_cache_hit_serves_chunked_prefill():
     ids_a = prompt + list(rng.integers(0, vocab, 20))
     ids_b = prompt + list(rng.integers(0, vocab, 20))
     bm = pa.BlockManager(NB, B, rng.permutation(NB))
-    gk = torch.zeros((NB, Hkv, B, D), dtype=torch.float16, device="cuda")
+    gk = torch.zeros(pa.key_shape(NB, Hkv, B, D, torch.float16), dtype=torch.float16, device="cuda")
     gv = torch.zeros((NB, Hkv, D, B), dtype=torch.float16, device="cuda")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
 
@@ -178,7 +178,7 @@ def test_prefix_cache_hit_serves_chunked_prefill():
 
     # Oracle: B's whole sequence recomputed into a pool of its own (identity table).
     k, v = kv(np.asarray(ids_b), 0)
-    kc = np.zeros((6, Hkv, B, D))
+    kc = np.zeros((6, Hkv, D // 32, B, 32))  # float16 key tiles: 32-element chunks
     vc = np.zeros((6, Hkv, D, B))
     oracle.reshape_and_cache(kc, vc, oracle.to_float64(k, dt), oracle.to_float64(v, dt), np.arange(len(ids_b)))
     ref = oracle.prefill_attention(oracle.to_float64(q, dt), np.array([0, 20]), kc, vc, np.arange(6)[None, :],
@@ -199,7 +199,7 @@ def test_scheduler_tables_drive_decode():
 
     B, D, Hkv, G, NB = 16, 64, 2, 4, 7
     rng = np.random.default_rng(77)
-    kc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), "f16")
+    kc = synth.key_chunks_of(synth.f32_to_storage(rng.standard_normal((NB, Hkv, B, D)).astype(np.float32), "f16"), 2)
     vc = synth.f32_to_storage(rng.standard_normal((NB, Hkv, D, B)).astype(np.float32), "f16")
     gk, gv = harness.to_device(kc, "f16"), harness.to_device(vc, "f16")
     bm = pa.BlockManager(NB, B, rng.permutation(NB))

@@ -127,14 +127,16 @@ def test_quantiser_on_every_binade_and_saturation():
     x[:1, 0, :] = np.resize(mids, D)
     x[1:2, 0, :] = -np.resize(mids[::-1], D)
     x[2, 0, :4] = [np.inf, -np.inf, 0.0, -0.0]
-    kc8 = torch.zeros((n // B, H, B, D), dtype=torch.uint8, device="cuda")
+    kc8 = torch.zeros(pa.key_shape(n // B, H, B, D, torch.uint8), dtype=torch.uint8, device="cuda")
     vc8 = torch.zeros((n // B, H, D, B), dtype=torch.uint8, device="cuda")
     xs = torch.from_numpy(x).cuda()
     slots = torch.arange(n, dtype=torch.int64, device="cuda")
     for scales in [(2.0**-6, 1.0), (0.0173, 3.1)]:
         pa.pa_reshape_and_cache(kc8, vc8, xs, xs, slots, scales=scales)
         torch.cuda.synchronize()
-        for got, sc, order in ((kc8, scales[0], (0, 2, 1, 3)), (vc8, scales[1], (0, 3, 1, 2))):
+        # Token rows: key tiles [n/B, H, D/64, B, 64] -> [n/B, B, H, D/64, 64];
+        # value tiles [n/B, H, D, B] -> [n/B, B, H, D].
+        for got, sc, order in ((kc8, scales[0], (0, 3, 1, 2, 4)), (vc8, scales[1], (0, 3, 1, 2))):
             g = got.cpu().numpy().transpose(*order).reshape(n, H, D)
             assert np.array_equal(g, oracle.fp8_quantize(x, sc)), scales
 
@@ -205,7 +207,8 @@ def test_fp8_rejections():
 
     w = synth.custom(seed=1, dtype="f16", num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, seq_lens=[20])
     gw = harness.GpuWorkload(w)
-    kc8 = torch.zeros(gw.key_cache.shape, dtype=torch.uint8, device="cuda")
+    NB, H, NC, B, KC = gw.key_cache.shape
+    kc8 = torch.zeros(pa.key_shape(NB, H, B, NC * KC, torch.uint8), dtype=torch.uint8, device="cuda")
     vc8 = torch.zeros(gw.value_cache.shape, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(gw.query)
     with pytest.raises(pa.PaError) as e:  # invalid scale

@@ -42,7 +42,7 @@ def _expected(w, slots, dt):
     T = len(slots)
     nk, nv = w.new_key[:T], w.new_value[:T]
     if dt == "fp8":
-        kc, vc = oracle.fp8_quantize(w.key_cache, FP8_SCALES[0]), oracle.fp8_quantize(w.value_cache, FP8_SCALES[1])
+        kc, vc = harness.fp8_pool_oracle(w, FP8_SCALES)
         oracle.reshape_and_cache_fp8(kc, vc, nk, nv, slots, *FP8_SCALES)
     else:
         kc, vc = w.key_cache.copy(), w.value_cache.copy()

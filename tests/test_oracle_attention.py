@@ -10,12 +10,14 @@ import oracle
 from paged_kv_cache_326_amd import synth
 
 
-def _identity_pool(Kd, Vd, B):
+def _identity_pool(Kd, Vd, B, kc_width=None):
     """Lay dense per-sequence K/V [S, L, Hkv, D] (L a multiple of B) into a
-    pool whose sequence s owns blocks s*nb .. s*nb+nb-1, by reshaping."""
+    pool whose sequence s owns blocks s*nb .. s*nb+nb-1, by reshaping (key
+    tiles in column chunks of kc_width dims, D // 2 by default)."""
     S, L, Hkv, D = Kd.shape
     nb = L // B
-    kc = Kd.reshape(S, nb, B, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(S * nb, Hkv, B, D)
+    KC = kc_width or max(D // 2, 1)
+    kc = Kd.reshape(S, nb, B, Hkv, D // KC, KC).transpose(0, 1, 3, 4, 2, 5).reshape(S * nb, Hkv, D // KC, B, KC)
     vc = Vd.reshape(S, nb, B, Hkv, D).transpose(0, 1, 3, 4, 2).reshape(S * nb, Hkv, D, B)  # value tiles [D][B]
     tables = np.arange(S * nb, dtype=np.int32).reshape(S, nb)
     return np.ascontiguousarray(kc), np.ascontiguousarray(vc), tables
@@ -89,7 +91,7 @@ def test_decode_shared_prefix_equals_private_copies():
 def test_decode_closed_forms():
     rng = np.random.default_rng(3)
     NB, Hkv, B, D, Hq = 6, 2, 4, 8, 4
-    kc = rng.standard_normal((NB, Hkv, B, D))
+    kc = rng.standard_normal((NB, Hkv, D // 4, B, 4))  # key tiles in 4-dim column chunks
     vc = rng.standard_normal((NB, Hkv, D, B))  # value tiles [D][B]
     tables = np.array([[3, 1, 5], [0, 2, 4]], np.int32)
     q = rng.standard_normal((2, Hq, D))
@@ -111,7 +113,7 @@ def test_decode_closed_forms():
     assert np.all(out[0] == 0) and np.all(np.isfinite(out[1]))
     # One dominant key: the weight concentrates on it.
     kd = np.zeros_like(kc)
-    kd[tables[0, 1], :, 2, :] = 1.0
+    kd[tables[0, 1], :, :, 2, :] = 1.0
     out = oracle.decode_attention(np.ones_like(q) * 100, kd, vc, tables, np.array([10, 10]), 1.0)
     np.testing.assert_allclose(out[0, 0], vc[tables[0, 1], 0, :, 2], atol=1e-12)
 
@@ -119,7 +121,7 @@ def test_decode_closed_forms():
 def test_decode_gqa_groups_are_contiguous_heads():
     # Hkv=2, Hq=4: heads 0,1 read KV head 0, heads 2,3 read KV head 1.
     rng = np.random.default_rng(4)
-    kc = rng.standard_normal((2, 2, 4, 8))
+    kc = rng.standard_normal((2, 2, 2, 4, 4))
     vc = np.zeros((2, 2, 8, 4))
     vc[:, 0] = 1.0
     vc[:, 1] = -1.0
@@ -266,3 +268,26 @@ def test_prefill_row_before_any_present_key_is_zero():
     assert (got[:B] == 0).all()
     for h in range(Hq):
         np.testing.assert_array_equal(got[B, h], Vd[0, B, 0])
+
+
+def test_key_tile_layout_round_trip_and_definition():
+    # Key element (block b, head h, offset t, dim d) lives at
+    # key_cache[b, h, d // kc, t, d % kc]; key_rows / key_tiles convert,
+    # checked element by element on a pool whose values name their position.
+    NB, H, B, D, KC = 3, 2, 4, 12, 4
+    rows = np.arange(NB * H * B * D, dtype=np.float64).reshape(NB, H, B, D)
+    tiles = oracle.key_tiles(rows, KC)
+    assert tiles.shape == (NB, H, D // KC, B, KC)
+    for b in range(NB):
+        for h in range(H):
+            for t in range(B):
+                for d in range(D):
+                    assert tiles[b, h, d // KC, t, d % KC] == rows[b, h, t, d]
+    np.testing.assert_array_equal(oracle.key_rows(tiles), rows)
+    # Memory order: within a tile, chunk after chunk, each chunk row after row.
+    flat = tiles[1, 0].reshape(-1)
+    np.testing.assert_array_equal(flat[:KC], rows[1, 0, 0, :KC])
+    np.testing.assert_array_equal(flat[KC:2 * KC], rows[1, 0, 1, :KC])
+    np.testing.assert_array_equal(flat[B * KC:B * KC + KC], rows[1, 0, 0, KC:2 * KC])
+    with pytest.raises(ValueError):
+        oracle.key_tiles(rows, 5)

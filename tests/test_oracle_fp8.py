@@ -114,12 +114,12 @@ def test_quantiser_error_bound_and_power_of_two_scale():
 def test_fp8_scatter_writes_quantised_codes():
     rng = np.random.default_rng(3)
     NB, H, B, D = 4, 2, 16, 8
-    kc = np.full((NB, H, B, D), 0x55, np.uint8)
+    kc = np.full((NB, H, 2, B, D // 2), 0x55, np.uint8)  # key tiles in 4-code chunks
     vc = np.full((NB, H, D, B), 0x55, np.uint8)
     key = rng.standard_normal((3, H, D)).astype(np.float16)
     val = rng.standard_normal((3, H, D)).astype(np.float16)
     slots = np.array([5, -1, 40])
     fp8.reshape_and_cache_fp8(kc, vc, key, val, slots, 0.05, 0.02)
-    assert np.array_equal(kc[0, :, 5], fp8.fp8_quantize(key[0], 0.05))
+    assert np.array_equal(kc[0, :, :, 5].reshape(H, D), fp8.fp8_quantize(key[0], 0.05))
     assert np.array_equal(vc[2, :, :, 8], fp8.fp8_quantize(val[2], 0.02))
     assert np.count_nonzero(kc != 0x55) <= 2 * H * D  # the padding token wrote nothing

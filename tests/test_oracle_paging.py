@@ -118,18 +118,18 @@ def test_reshape_and_cache_round_trip_and_sentinel():
         np.testing.assert_array_equal(Kg, K[cu[s] : cu[s + 1]])
         np.testing.assert_array_equal(Vg, V[cu[s] : cu[s + 1]])
     # Exactly T slots changed in each pool; the rest keep the sentinel.
-    changed = (kc != -7.0).all(axis=(1, 3))  # [NB, B]
+    changed = (kc != -7.0).all(axis=(1, 2, 4))  # key tiles [NB, H, D // kc, B, kc] -> [NB, B]
     assert changed.sum() == T
     assert ((vc != -9.0).all(axis=(1, 2))).sum() == T  # value tiles [D][B]: the slot is the last axis
 
 
 def test_reshape_and_cache_skips_negative_and_rejects_duplicates():
-    kc = np.zeros((4, 2, 4, 3))
+    kc = np.zeros((4, 2, 3, 4, 1))  # key tiles in 1-dim chunks: [NB, H, D, B, 1]
     vc = np.zeros((4, 2, 3, 4))
     K = np.ones((3, 2, 3))
     V = 2 * np.ones((3, 2, 3))
     oracle.reshape_and_cache(kc, vc, K, V, np.array([5, -1, 15]))
-    assert kc[1, :, 1].sum() == 6 and kc[3, :, 3].sum() == 6 and kc.sum() == 12
+    assert kc[1, :, :, 1].sum() == 6 and kc[3, :, :, 3].sum() == 6 and kc.sum() == 12
     assert vc.sum() == 24
     with pytest.raises(ValueError):
         oracle.reshape_and_cache(kc, vc, K, V, np.array([5, 5, 2]))
