@@ -11,9 +11,10 @@
 // (partition, KV head, sequence): a partition is `partition` consecutive
 // tokens of the sequence (a multiple of the block size).  All G query heads
 // that share the KV head are served together, so every K/V byte is read from
-// HBM once.  The partition is cut into steps of 32 tokens; wave w takes steps
-// w, w + kNW, ... and keeps the next steps' K/V loads in flight (a register
-// ring) while it computes the current one.
+// HBM once.  The partition is cut into steps of 32 tokens, dealt to the waves
+// round-robin (rotated so that the partition's last step falls to wave 0);
+// each wave keeps its next steps' K/V loads in flight (a register ring)
+// while it computes the current one.
 //
 // Per step, with the G heads as the 16-wide N side of v_mfma_f32_16x16x*
 // (heads G..15 are zero columns):
@@ -316,25 +317,52 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();  // table slice visible
 
-  // Fused append: in the workgroup whose partition holds the sequence's last
-  // position, the wave that will process the partition's last step writes
-  // this step's token (KV head g) into its slot, exactly as the scatter
-  // does, and waits until its stores have completed before it issues any
-  // load; no other wave reads that token's block (the last block belongs to
-  // the last step only), so the other waves start streaming at once.
+  // Steps go to the waves round-robin, rotated so that the partition's last
+  // step (which holds a sequence's newest position) falls to wave 0, the
+  // first wave on its SIMD: the first wave of each SIMD issues ahead of the
+  // second (on the benchmark layer waves 0-3 finish their steps about 9 us
+  // before waves 4-7), so the appending wave's wait below costs nothing.
   const int nsteps = (ntok + kStep - 1) / kStep;
-  if (a.new_key != nullptr && ntok > 0 && tok0 + ntok == L && w == (nsteps - 1) % kNW) {
-    using S = typename Src<T>::type;
+  const int rot = nsteps > 0 ? (kNW - (nsteps - 1) % kNW) % kNW : 0;
+  const int first = (w + kNW - rot) % kNW;  // this wave's steps: first, first + kNW, ...
+
+  // Fused append: in the workgroup whose partition holds the sequence's last
+  // position, wave 0 (which processes the partition's last step) writes this
+  // step's token (KV head g) into its slot, exactly as the scatter does.
+  // The key row is stored now, and the wave waits until those stores have
+  // completed before it issues any load; no other wave reads that token's
+  // block (the last block belongs to the last step only), so the other
+  // waves start streaming at once.  The value row is a column of the
+  // transposed value tile, i.e. head_dim scattered element stores; instead
+  // the wave patches it into the block's value tile once it has loaded that
+  // tile for its last step, and writes the tile back whole (every other slot
+  // bit for bit as loaded), which the memory system takes as full lines.
+  using S = typename Src<T>::type;
+  const int jnew = ntok > 0 ? (ntok - 1) / B : 0;  // the new token's block in the table slice
+  const bool apnd = a.new_key != nullptr && ntok > 0 && tok0 + ntok == L && w == 0 && s_bt[jnew] >= 0;
+  uint32_t nvb[NDT];  // the new value's element for dims 16 dd + r (storage bits)
+  if (a.new_key != nullptr && ntok > 0 && tok0 + ntok == L && w == 0) {
     constexpr int VS = vec16<S>();
     constexpr int NCH = D / VS;  // 16-byte source chunks per row
-    static_assert(2 * NCH <= 64, "one wave writes the token");
-    const int pb = s_bt[(ntok - 1) / B];
+    static_assert(NCH <= 64, "one wave writes the key row");
+    const int pb = s_bt[jnew];
     const int off = (L - 1) % B;
-    if (lane < 2 * NCH && pb >= 0) {
-      const int which = lane / NCH, c = lane % NCH;
-      const S* src = reinterpret_cast<const S*>(which ? a.new_value : a.new_key) + ((int64_t)s * Hkv + g) * D + c * VS;
-      store_kv_chunk<T>(reinterpret_cast<T*>(a.cache.key_cache), reinterpret_cast<T*>(a.cache.value_cache), which, pb,
-                        off, g, c, VS, Hkv, D, B, *reinterpret_cast<const u32x4*>(src), a.cache.k_scale,
+    const S* vrow = reinterpret_cast<const S*>(a.new_value) + ((int64_t)s * Hkv + g) * D;
+#pragma unroll
+    for (int dd = 0; dd < NDT; ++dd) {
+      const S x = vrow[16 * dd + r];
+      if constexpr (kFp8) {
+        nvb[dd] = f32_to_e4m3((float)x / a.cache.v_scale);
+      } else if constexpr (kF32) {
+        nvb[dd] = __float_as_uint(x);
+      } else {
+        nvb[dd] = __builtin_bit_cast(uint16_t, x);
+      }
+    }
+    if (lane < NCH && pb >= 0) {
+      const S* src = reinterpret_cast<const S*>(a.new_key) + ((int64_t)s * Hkv + g) * D + lane * VS;
+      store_kv_chunk<T>(reinterpret_cast<T*>(a.cache.key_cache), reinterpret_cast<T*>(a.cache.value_cache), 0, pb,
+                        off, g, lane, VS, Hkv, D, B, *reinterpret_cast<const u32x4*>(src), a.cache.k_scale,
                         a.cache.v_scale);
     }
     if (lane == 0 && g == 0) a.slots[s] = pb >= 0 ? (int64_t)pb * B + off : -1;
@@ -361,16 +389,25 @@ decode_partition_kernel(DecodeArgs a) {
       const int pb = (t < ntok && j < nbp) ? s_bt[j] : -1;
       // Key load ls reads 64-byte chunk ls of the 16 rows: rows 8(r/4) +
       // 4c .. +3 are adjacent in a chunk, so the wave reads whole 128-byte
-      // lines, each once; K and V are streamed with non-temporal loads.
+      // lines, each once.  K and V are streamed with non-temporal loads,
+      // except FP8 keys: ordinary loads measured faster there (28.4 against
+      // 29.8 us on the benchmark layer).
       const T* src = kbase + (int64_t)pb * blk_stride + (t % B) * KC + CE * grp;
 #pragma unroll
-      for (int ls = 0; ls < NLK; ++ls)
-        b.k[c][ls] = pb >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)ls * B * KC))
-                             : u32x4{0, 0, 0, 0};
+      for (int ls = 0; ls < NLK; ++ls) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(src + (int64_t)ls * B * KC);
+        if constexpr (kFp8)
+          b.k[c][ls] = pb >= 0 ? *p : u32x4{0, 0, 0, 0};
+        else
+          b.k[c][ls] = pb >= 0 ? __builtin_nontemporal_load(p) : u32x4{0, 0, 0, 0};
+      }
     }
     const int t0 = stok + 8 * grp;
     const int j = t0 / B;
-    const int pb = (t0 < ntok && j < nbp) ? s_bt[j] : -1;
+    // The appending wave loads the new token's whole block in its last step
+    // (past the sequence's end too): it writes that value tile back.
+    const bool whole = apnd && st == nsteps - 1 && j == jnew;
+    const int pb = ((t0 < ntok || whole) && j < nbp) ? s_bt[j] : -1;
     const T* vsrc = vbase + (int64_t)pb * blk_stride + r * B + (t0 % B);
 #pragma unroll
     for (int dd = 0; dd < NDT; ++dd) {
@@ -455,6 +492,42 @@ decode_partition_kernel(DecodeArgs a) {
       for (int dd = 0; dd < NDT; ++dd) o[dd] *= alpha;
     }
 
+    // The appending wave's last step: put the new token's value into the
+    // loaded value tile of its block and store the tile's pieces back.
+    if (apnd && st == nsteps - 1 && t0 / B == jnew) {
+      const int e = (ntok - 1) - t0;  // the new token's place in this lane's 8 tokens, if 0..7
+      T* vdst = reinterpret_cast<T*>(a.cache.value_cache) + (int64_t)g * D * B +
+                (int64_t)s_bt[jnew] * blk_stride + r * B + (t0 % B);
+#pragma unroll
+      for (int dd = 0; dd < NDT; ++dd) {
+        // Selects over the words (a runtime index into the register array
+        // would move it to scratch memory).
+#pragma unroll
+        for (int q = 0; q < VW; ++q) {
+          if constexpr (VW == 8) {
+            b.v[dd][q] = q == e ? nvb[dd] : b.v[dd][q];
+          } else if constexpr (VW == 4) {
+            const uint32_t sh = 16u * (uint32_t)(e & 1);
+            const uint32_t put = (b.v[dd][q] & ~(0xffffu << sh)) | (nvb[dd] << sh);
+            b.v[dd][q] = (e >= 0 && q == (e >> 1)) ? put : b.v[dd][q];
+          } else {
+            const uint32_t sh = 8u * (uint32_t)(e & 3);
+            const uint32_t put = (b.v[dd][q] & ~(0xffu << sh)) | (nvb[dd] << sh);
+            b.v[dd][q] = (e >= 0 && q == (e >> 2)) ? put : b.v[dd][q];
+          }
+        }
+        T* p = vdst + dd * 16 * B;
+        if constexpr (VW == 8) {
+          reinterpret_cast<u32x4*>(p)[0] = u32x4{b.v[dd][0], b.v[dd][1], b.v[dd][2], b.v[dd][3]};
+          reinterpret_cast<u32x4*>(p)[1] = u32x4{b.v[dd][4], b.v[dd][5], b.v[dd][6], b.v[dd][7]};
+        } else if constexpr (VW == 4) {
+          *reinterpret_cast<u32x4*>(p) = u32x4{b.v[dd][0], b.v[dd][1], b.v[dd][2], b.v[dd][3]};
+        } else {
+          *reinterpret_cast<u32x2*>(p) = u32x2{b.v[dd][0], b.v[dd][1]};
+        }
+      }
+    }
+
     // Value tokens past the end (or in a block outside the pool) are zeroed:
     // their probabilities are 0 and 0 * NaN would poison the sums.
     if (nvalid < 8) {
@@ -530,19 +603,19 @@ decode_partition_kernel(DecodeArgs a) {
     l_run = l_run * alpha + lstep;
   };
 
-  // 3. The wave's steps w, w + kNW, ..., NBUF of them in flight.
-  const int nmine = nsteps > w ? (nsteps - w + kNW - 1) / kNW : 0;
+  // 3. The wave's steps first, first + kNW, ..., NBUF of them in flight.
+  const int nmine = nsteps > first ? (nsteps - first + kNW - 1) / kNW : 0;
   Buf buf[NBUF];
 #pragma unroll
   for (int i = 0; i < NBUF; ++i)
-    if (i < nmine) load(buf[i], w + i * kNW);
+    if (i < nmine) load(buf[i], first + i * kNW);
   for (int i0 = 0; i0 < nmine; i0 += NBUF) {
 #pragma unroll
     for (int bi = 0; bi < NBUF; ++bi) {
       const int i = i0 + bi;
       if (i < nmine) {
-        compute(buf[bi], w + i * kNW);
-        if (i + NBUF < nmine) load(buf[bi], w + (i + NBUF) * kNW);
+        compute(buf[bi], first + i * kNW);
+        if (i + NBUF < nmine) load(buf[bi], first + (i + NBUF) * kNW);
       }
     }
   }
