@@ -14,16 +14,17 @@ every per-step tensor) are rotated so that successive steps cannot be served
 from the 256 MB last-level cache.
 
 Prints one JSON line.  ``value`` is attended KV tokens per second for the
-whole step, from a timed run of plain steps; ``roofline`` reports the
-decode call's algorithmic bytes over the duration of its dominant launch,
-the partition kernel, from a second timed run of the same steps in which
-every partition kernel records its own start and end into HIP events
+whole step, from a timed run of plain back-to-back steps; ``roofline``
+reports the algorithmic bytes over the duration of the dominant launch, the
+partition kernel, from a second timed run of the same steps in which every
+partition kernel records its own start and end into HIP events
 (hipExtLaunchKernel: no marker packet enters the stream; such self-timed
-launches cost the step about 6 us, which is why ``value`` is taken from the
-plain run), against 8 TB/s; the whole decode call, merge included, is
-timed separately and reported beside it;
+launches cost the step a few microseconds, which is why ``value`` is taken
+from the plain run), against 8 TB/s, and beside it the whole decode call
+(``decode_call_*``, back-to-back calls between two events) and the step;
+``secondary`` times the other workloads the same way (back-to-back calls);
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.
+workload, with single-thread and prefill legs.
 """
 
 from __future__ import annotations
@@ -38,6 +39,10 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# Kernel arguments in device memory (the HIP default on MI355X boxes we ran
+# on; with them in host memory every launch waits on a host round trip:
+# measured 5 us per decode step).  Set before the HIP runtime starts.
+os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -153,19 +158,22 @@ def prefill_flops(w) -> int:
     return 4 * w.head_dim * w.num_heads * pairs
 
 
-def _median_us(fn, iters=50, warm=5):
+def _burst_us(fn, iters=100, warm=10):
+    """Mean microseconds per call of ``iters`` back-to-back calls between two
+    events (no event between the calls: an event pair around every call adds
+    about 2 us to each on this GPU)."""
     import torch
 
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
         fn(i)
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return a.elapsed_time(b) * 1e3 / iters
 
 
 def _copies(w, n):
@@ -194,7 +202,7 @@ def secondary(copies_n: int):
         w = synth.config(k, poison_unused=False)
         cs = _copies(w, copies_n)
         ws = [pa.decode_workspace(c.query, c.key_cache, w.max_seq_len) for c in cs]
-        t = _median_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
+        t = _burst_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
         # The same batch with the host plan (only partitions that hold tokens,
         # longest first), as a scheduler that knows the lengths would call it.
         Pk = pa.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, w.max_seq_len, w.block_size)
@@ -205,7 +213,7 @@ def secondary(copies_n: int):
             pa.pa_decode_run(c.out, c.query, c.key_cache, c.value_cache, c.block_tables, c.seq_lens, w.scale,
                              w.max_seq_len, workspace=ws[i % len(cs)], partition_size=Pk, work=work)
 
-        tp = _median_us(planned)
+        tp = _burst_us(planned)
         nb = algorithmic_decode_bytes(w)
         uniq = int((w.refcounts > 0).sum()) * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes * 2
         res[synth.CONFIG_NAMES[k]] = {
@@ -213,6 +221,9 @@ def secondary(copies_n: int):
             "frac_of_hbm_peak": round(nb / t / 1e3 / HBM_PEAK_GBS, 4),
             "attended_tokens_per_s": int(w.seq_lens.sum()) / (t * 1e-6),
             "unique_kv_bytes": uniq, "dtype": w.dtype,
+            # HBM-honest rate: blocks shared by several sequences are read
+            # from memory once (the rest of the logical bytes come from caches).
+            "unique_GBps": round(uniq / t / 1e3, 1), "unique_frac_of_hbm_peak": round(uniq / t / 1e3 / HBM_PEAK_GBS, 4),
             "planned_decode_us": round(tp, 2), "planned_GBps": round(nb / tp / 1e3, 1),
             "planned_frac_of_hbm_peak": round(nb / tp / 1e3 / HBM_PEAK_GBS, 4),
             "planned_units": int(work.numel()),
@@ -229,11 +240,11 @@ def secondary(copies_n: int):
     gps = [harness.GpuWorkload(wp).share_pool(c) for c in cs]
     gds = [harness.GpuWorkload(wd).share_pool(c) for c in cs]
     wsd = [pa.decode_workspace(g.query, g.key_cache, wd.max_seq_len) for g in gds]
-    tp = _median_us(lambda i: gps[i % len(gps)].prefill(), iters=20)
-    td = _median_us(lambda i: gds[i % len(gds)].decode(workspace=wsd[i % len(gds)]))
+    tp = _burst_us(lambda i: gps[i % len(gps)].prefill(), iters=20)
+    td = _burst_us(lambda i: gds[i % len(gds)].decode(workspace=wsd[i % len(gds)]))
     # The step's scatter: slot mapping + reshape_and_cache of all 2096 new
     # tokens (4 x 512 chunk tokens and 48 decode tokens) in one launch.
-    ta = _median_us(lambda i: cs[i % len(cs)].append())
+    ta = _burst_us(lambda i: cs[i % len(cs)].append())
     fl = prefill_flops(wp)
     nbd = algorithmic_decode_bytes(wd)
     nba = 4 * w.num_new_tokens * w.num_kv_heads * w.head_dim * w.elem_bytes + 8 * w.num_new_tokens
@@ -253,7 +264,7 @@ def secondary(copies_n: int):
     for name, ww in (("permuted", w), ("identity", synth.identity_tables(w))):
         cs = _copies(ww, copies_n)
         ws = [pa.decode_workspace(c.query, c.key_cache, ww.max_seq_len) for c in cs]
-        out[name] = _median_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
+        out[name] = _burst_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
         del cs, ws
         torch.cuda.empty_cache()
     res["block_table_indirection"] = {
@@ -278,7 +289,7 @@ def secondary(copies_n: int):
         pa.pa_decode(c.out, c.query, kc8, vc8, c.block_tables, c.seq_lens, w.scale, w.max_seq_len, workspace=ws,
                      scales=scales)
 
-    t8 = _median_us(fp8_decode)
+    t8 = _burst_us(fp8_decode)
     nb8 = algorithmic_decode_bytes(w, kv_elem_bytes=1)
     res["fp8_e4m3_" + synth.CONFIG_NAMES[2]] = {
         "decode_us": round(t8, 2), "algorithmic_bytes": nb8, "GBps": round(nb8 / t8 / 1e3, 1),
@@ -308,7 +319,7 @@ def secondary(copies_n: int):
         pa.pa_prefill_chunk(g.out, g.query, kc8, vc8, g.cu_q_lens, g.seq_lens, g.block_tables, wp.scale,
                             int(wp.q_lens.max()), scales=scales)
 
-    tpf = _median_us(fp8_prefill, iters=20)
+    tpf = _burst_us(fp8_prefill, iters=20)
     fl = prefill_flops(wp)
     res["fp8_e4m3_" + synth.CONFIG_NAMES[5] + "_prefill"] = {
         "prefill_us": round(tpf, 2), "prefill_flops": fl, "prefill_TFLOPs": round(fl / tpf / 1e6, 1),
@@ -318,7 +329,31 @@ def secondary(copies_n: int):
     del pf
     torch.cuda.empty_cache()
     res["block_moves"] = block_moves()
+    res["streaming_read_ceiling"] = stream_ceiling(algorithmic_decode_bytes(synth.config(2, poison_unused=False)),
+                                                   copies_n)
     return res
+
+
+def stream_ceiling(nbytes: int, copies_n: int = 3):
+    """A plain streaming read of ``nbytes`` (pa_stream_read, 16-byte
+    non-temporal loads) at the decode kernel's launch shape on the benchmark
+    layer (one 8-wave workgroup per compute unit) and at two wider shapes,
+    over rotated buffers: the read bandwidth a kernel that only reads these
+    bytes reaches, against which the decode call is set."""
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies_n)]
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    out = {"bytes": nbytes, "buffers": copies_n}
+    for wg, th in ((256, 512), (512, 512), (1024, 256)):
+        t = _burst_us(lambda i: pa.pa_stream_read(bufs[i % copies_n], wg, th, sink), iters=100)
+        out[f"{wg}x{th}_us"] = round(t, 2)
+        out[f"{wg}x{th}_GBps"] = round(nbytes / t / 1e3, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return out
 
 
 def block_moves(n: int = 1024):
@@ -349,7 +384,7 @@ def block_moves(n: int = 1024):
         ("swap_out_pinned_host", lambda i: pa.pa_gather_blocks(kc, vc, src, hk, hv), 10),
         ("swap_in_pinned_host", lambda i: pa.pa_scatter_blocks(kc, vc, dst, hk, hv), 10),
     ):
-        t = _median_us(fn, iters=it)
+        t = _burst_us(fn, iters=it)
         out[name + "_us"] = round(t, 1)
         if "host" in name:  # bound by the host link: bytes over the link per second
             out[name + "_link_GBps"] = round(moved / t / 1e3, 1)
@@ -389,7 +424,7 @@ def prefill_only(steps: int, warmup: int, copies_n: int, fp8: bool):
 
     for i in range(warmup):
         run(i)
-    t = _median_us(run, iters=steps)
+    t = _burst_us(run, iters=steps)
     fl = prefill_flops(wp)
     return {
         "workload": synth.CONFIG_NAMES[5] + "_prefill" + ("_fp8_e4m3" if fp8 else ""),
@@ -425,7 +460,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
         spent += time.perf_counter() - t0
         reps += 1
     toks = int(w.seq_lens.sum()) * reps
-    return {
+    out = {
         "value": toks / spent,
         "unit": "tokens/s",
         "cores": int(threads),
@@ -433,6 +468,47 @@ def cpu_baseline(w, budget_s: float = 12.0):
         "sample": f"{reps} full step(s) of the same workload (slot mapping, scatter, float64 decode of all "
                   f"{w.num_seqs} sequences) in {spent:.1f} s; host has {os.cpu_count()} logical CPUs",
     }
+    out["legs"] = oracle_legs()
+    return out
+
+
+def oracle_legs():
+    """The oracle's own timings beside the main baseline: float64 decode of
+    the tiny and the benchmark configs with one BLAS thread and with all of
+    them (median of 3 calls), and one call of the mixed config's chunked
+    prefill (4 x 512 queries over 3584 cached tokens) with all threads."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    from paged_kv_cache_326_amd import synth
+
+    legs = {}
+    for k in (1, 2):
+        w = synth.config(k, poison_unused=False)
+        dt = w.dtype
+        q, kc, vc = (oracle.to_float64(x, dt) for x in (w.query, w.key_cache, w.value_cache))
+        for label, limit in (("1_thread", 1), ("all_threads", None)):
+            ts = []
+            with threadpool_limits(limit):
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    oracle.decode_attention(q, kc, vc, w.block_tables, w.seq_lens, w.scale)
+                    ts.append(time.perf_counter() - t0)
+            t = float(np.median(ts))
+            legs[f"{synth.CONFIG_NAMES[k]}_decode_{label}"] = {
+                "s": round(t, 5), "attended_tokens_per_s": round(int(w.seq_lens.sum()) / t, 1),
+                "GBps_equivalent": round(algorithmic_decode_bytes(w) / t / 1e9, 3)}
+    w = synth.config(5, poison_unused=False)
+    pre, _ = synth.prefill_decode_split(w)
+    wp = w.subset(pre)
+    kc, vc = oracle.to_float64(w.key_cache, w.dtype), oracle.to_float64(w.value_cache, w.dtype)
+    t0 = time.perf_counter()
+    oracle.prefill_attention(oracle.to_float64(wp.query, wp.dtype), wp.cu_q_lens, kc, vc, wp.block_tables,
+                             wp.seq_lens, wp.scale)
+    t = time.perf_counter() - t0
+    legs[f"{synth.CONFIG_NAMES[5]}_prefill_all_threads_once"] = {
+        "s": round(t, 3), "TFLOPs_equivalent": round(prefill_flops(wp) / t / 1e12, 4)}
+    return legs
 
 
 def main():
@@ -448,6 +524,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
     ap.add_argument("--prefill", choices=("bf16", "fp8"), default=None,
                     help="time only the mixed config's chunked prefill (for counter collection)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="instead: time a plain streaming read of the benchmark layer's bytes at several launch shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     ap.add_argument("--write-traffic-record", metavar="DIR", default=None,
@@ -488,6 +566,10 @@ def main():
 
     if args.prefill:
         print(json.dumps(prefill_only(args.steps, args.warmup, args.copies, args.prefill == "fp8")), flush=True)
+        return
+    if args.stream_ceiling:
+        nb = algorithmic_decode_bytes(synth.config(2, poison_unused=False))
+        print(json.dumps({"streaming_read_ceiling": stream_ceiling(nb, args.copies)}), flush=True)
         return
 
     w = synth.config(args.config, poison_unused=False)
@@ -543,17 +625,9 @@ def main():
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     part_avg_s = float(part_ms.mean()) * 1e-3
     # The whole decode call (partition kernel, merge and the gap between
-    # them), timed apart from the step loop with events around the call.
-    for i in range(5):
-        copies[i % len(copies)].decode(partition_size=P, workspace=ws[i % len(copies)])
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-    for i, (a, b) in enumerate(cev):
-        a.record(stream)
-        copies[i % len(copies)].decode(partition_size=P, workspace=ws[i % len(copies)])
-        b.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in cev])
-    dec_avg_s = float(dec_ms.mean()) * 1e-3
+    # them, no new token written), as back-to-back calls between two events.
+    dec_avg_s = _burst_us(lambda i: copies[i % len(copies)].decode(partition_size=P, workspace=ws[i % len(copies)]),
+                          iters=100) * 1e-6
 
     attended = int(w.seq_lens.sum())
     nbytes = algorithmic_decode_bytes(w)
@@ -589,8 +663,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partition_kernel of pa_decode_append (new token written, attention over the "
-                      "partition; the merge kernel follows)",
+            "kernel": "decode_partition_kernel of pa_decode_append alone (new token written, attention over the "
+                      "partition), self-timed; the whole call, merge kernel included, is decode_call_*",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -601,9 +675,11 @@ def main():
             "kernel_us_median": float(np.median(part_ms)) * 1e3,
             "kernel_us_p10": float(np.percentile(part_ms, 10)) * 1e3,
             "kernel_us_p90": float(np.percentile(part_ms, 90)) * 1e3,
-            "decode_call_us_mean": float(dec_ms.mean()) * 1e3,
+            "decode_call_us": dec_avg_s * 1e6,
             "decode_call_GBps": nbytes / dec_avg_s / 1e9,
             "decode_call_frac": nbytes / dec_avg_s / 1e9 / HBM_PEAK_GBS,
+            "step_GBps": nbytes_kernel / (ms_per_step * 1e-3) / 1e9,
+            "step_frac": nbytes_kernel / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
         "attended_kv_tokens_per_s_decode": attended / dec_avg_s,
     }

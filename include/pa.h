@@ -516,6 +516,17 @@ int32_t pa_sched_generated(pa_scheduler* sched, int64_t request_id);
 int32_t pa_sched_num_waiting(pa_scheduler* sched);
 int32_t pa_sched_num_active(pa_scheduler* sched);
 
+/* Measurement helper, not part of the attention path: a plain streaming
+ * read of `bytes` bytes of device memory at `src` (16-byte aligned, bytes a
+ * multiple of 16) by `workgroups` workgroups of `threads` threads (a
+ * multiple of 64, at most 1024), each reading one contiguous share with
+ * 16-byte non-temporal loads, two batches of eight per thread in flight.
+ * sink: device uint32 [workgroups], XOR-ed with what each workgroup read
+ * (so the loads are kept).  Timing it beside pa_decode on the same number
+ * of bytes gives the read bandwidth the chip reaches at a launch shape. */
+pa_status pa_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads, uint32_t* sink,
+                         hipStream_t stream);
+
 const char* pa_status_string(pa_status status);
 const char* pa_version(void);
 

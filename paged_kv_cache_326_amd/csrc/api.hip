@@ -360,6 +360,16 @@ pa_status pa_decode_noalloc(const pa_kv_cache* cache, void* out, const void* que
   return decode_run(&d, stream);
 }
 
+pa_status pa_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t threads, uint32_t* sink,
+                         hipStream_t stream) {
+  if (workgroups <= 0 || threads <= 0 || threads > 1024 || threads % 64 || bytes % 16) return PA_ERR_SHAPE;
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return PA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(src) % 16) return PA_ERR_SHAPE;
+  const hipError_t e = pa::launch_stream_read(src, (int64_t)bytes, workgroups, threads, sink, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 pa_status pa_decode_ex(const pa_kv_cache* cache, void* out, const void* query, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                        int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,

@@ -80,6 +80,11 @@ hipError_t launch_block_move(const KvCacheArgs& c, const int32_t* src, const int
 // stage 1: partition kernel; 2: merge of the partials; 0: both.
 hipError_t launch_decode(const DecodeArgs& a, int stage, hipStream_t stream);
 
+// A plain streaming read of `bytes` (a multiple of 16) by `workgroups`
+// workgroups of `threads` threads; sink[w] receives workgroup w's XOR.
+hipError_t launch_stream_read(const void* src, int64_t bytes, int workgroups, int threads, uint32_t* sink,
+                              hipStream_t stream);
+
 // Query positions one prefill workgroup covers for a head group of `group`.
 int prefill_positions_per_tile(int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

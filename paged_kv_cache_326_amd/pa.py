@@ -95,6 +95,7 @@ EXPORTS = (
     "pa_decode_plan",
     "pa_decode_noalloc",
     "pa_prefill_chunk",
+    "pa_stream_read",
     "pa_copy_blocks",
     "pa_gather_blocks",
     "pa_scatter_blocks",
@@ -239,6 +240,8 @@ def lib() -> ctypes.CDLL:
     for name in ("pa_sched_num_waiting", "pa_sched_num_active"):
         getattr(L, name).argtypes = [sc]
         getattr(L, name).restype = i32
+    L.pa_stream_read.argtypes = [vp, sz, i32, i32, vp, vp]
+    L.pa_stream_read.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -773,6 +776,19 @@ class Scheduler:
 
     def num_active(self) -> int:
         return int(lib().pa_sched_num_active(self._h))
+
+
+def pa_stream_read(src: torch.Tensor, workgroups: int, threads: int, sink: torch.Tensor, stream=None):
+    """Measurement helper: a plain streaming read of ``src`` (all its bytes)
+    at the given launch shape; ``sink`` is a uint32/int32 device tensor of at
+    least ``workgroups`` words (XOR-ed)."""
+    _need(src, "src")
+    _need(sink, "sink")
+    if sink.numel() < workgroups or sink.element_size() != 4:
+        raise ValueError("sink needs one 32-bit word per workgroup")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().pa_stream_read(src.data_ptr(), nbytes, int(workgroups), int(threads), sink.data_ptr(),
+                                _stream(stream)), "pa_stream_read")
 
 
 def version() -> str:

@@ -204,3 +204,15 @@ def test_decode_noalloc_refuses_oversize_batches_on_the_host(L):
     assert L.pa_decode_noalloc(None, 0x3000, 0x4000, 0x5000, 500, 0x6000, 64, 32, 8000, 0.1, 16, None) == 1
     assert L.pa_decode_noalloc(ctypes.byref(_cache(pa, head_dim=96)), 0x3000, 0x4000, 0x5000, 4, 0x6000, 4, 8, 50,
                                0.1, 0, None) == 3
+
+
+def test_stream_read_rejects_bad_shapes_on_the_host(L):
+    # The measurement helper checks its launch shape before launching.
+    assert L.pa_stream_read(0x1000, 1 << 20, 0, 256, 0x2000, None) == 2   # no workgroups
+    assert L.pa_stream_read(0x1000, 1 << 20, 4, 100, 0x2000, None) == 2   # not whole waves
+    assert L.pa_stream_read(0x1000, 1 << 20, 4, 2048, 0x2000, None) == 2  # over 1024 threads
+    assert L.pa_stream_read(0x1000, 1000, 4, 256, 0x2000, None) == 2      # not 16-byte pieces
+    assert L.pa_stream_read(0x1008, 1 << 20, 4, 256, 0x2000, None) == 2   # misaligned
+    assert L.pa_stream_read(0, 1 << 20, 4, 256, 0x2000, None) == 1
+    assert L.pa_stream_read(0x1000, 1 << 20, 4, 256, 0, None) == 1
+    assert L.pa_stream_read(0x1000, 0, 4, 256, 0x2000, None) == 0         # nothing to read
