@@ -33,6 +33,21 @@ DEVICE_FLAGS = [
 ]
 
 
+# Extra device flags per source.  The 16-bit prefill kernel keeps its matrix
+# products' accumulators in ordinary vector registers (LLVM's VGPR form of
+# the MFMA instructions): with them in the accumulator file, the compiler
+# copies the whole accumulator set around the tile loop's rarely taken
+# branches, and every softmax read of the scores becomes a register move.
+FILE_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def device_flags(src: str) -> list:
+    """hipcc flags for one HIP source of the library."""
+    return [*DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), [])]
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -46,7 +61,7 @@ def _compile(src: str, verbose: bool) -> str:
         cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"),
                "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
     else:
-        cmd = [hipcc(), *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+        cmd = [hipcc(), *device_flags(src), "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

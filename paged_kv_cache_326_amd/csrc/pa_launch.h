@@ -85,8 +85,11 @@ hipError_t launch_decode(const DecodeArgs& a, int stage, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, int64_t bytes, int workgroups, int threads, uint32_t* sink,
                               hipStream_t stream);
 
-// Query positions one prefill workgroup covers for a head group of `group`.
+// Query positions one prefill workgroup covers for a head group of `group`
+// (the same for every pool dtype).
 int prefill_positions_per_tile(int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The FP8-pool kernel (prefill_fp8.hip); launch_prefill dispatches to it.
+hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -1,4 +1,5 @@
-// Chunked-prefill attention over the paged cache on gfx950 matrix cores.
+// Chunked-prefill attention over a float16 / bfloat16 paged cache on gfx950
+// matrix cores (FP8 pools: prefill_fp8.hip).
 //
 // Sources: [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践",
 // section "工程边界与架构取舍" (prefill is a compute-bound matrix product; a
@@ -10,20 +11,31 @@
 // (ctx = seq_len - q_s; the chunk's own K/V are already in the pool) and
 // attends causally: position ctx+i sees keys 0 .. ctx+i.
 //
-// Work decomposition.  A workgroup (8 waves) owns 256 query rows that share
-// one KV head: the G heads of the group times 256/G consecutive positions.
-// Each wave owns 32 rows.  Keys stream through in tiles of 32: the tile's K
-// rows ([32][D]) and V^T ([D][32], as the pool stores value tiles) are staged
-// in LDS, then per wave
+// Work decomposition.  A workgroup of 4 waves (one per SIMD) owns 256 query
+// rows that share one KV head: the G heads of the group times 256/G
+// consecutive positions.  Each wave owns 64 rows as two halves of 32, so
+// every K or V operand read from LDS feeds two matrix products (LDS traffic
+// per flop is half that of 32-row waves).  Keys stream through in tiles of
+// 32; per wave and half
 //   S^T[32 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16 over D
 //   online softmax down each column (a column is one query row, held by a
 //   lane pair), P^T rounded to the storage type in registers
 //   O^T[D x 32 rows]     += V^T . P^T    v_mfma_f32_32x32x16 over the tile
-// The loop is software-pipelined so that matrix and vector work of one wave
-// overlap: while tile t's softmax runs on the vector ALU, the scores of tile
-// t+1 are computed on the matrix cores.  LDS holds three tile stages (t,
-// t+1 and t+2, written while t is used), and a ring of register sets keeps
-// the global loads of later tiles in flight.
+// With one wave per SIMD the matrix and vector work overlap inside the wave:
+// each iteration multiplies the scores of tile t+1 while it exponentiates
+// and rounds tile t's probabilities, then runs tile t's PV product while it
+// finds tile t+1's maxima and rescale factors.  Tiles whose keys need masks
+// (the causal diagonal, blocks missing from the pool), a rescale of the
+// accumulators, or the rounding remainder below take a slower, generic path.
+//
+// Staging.  Tiles move from the pool straight into LDS (16 bytes per lane,
+// no registers on the way), four stages deep: while tiles t and t+1 are
+// read, tile t+2 has landed and tile t+3 is in flight.  A stage holds the
+// tile's K as the pool stores it (column chunks of 32 dimensions, one
+// 64-byte row per key) and its V^T (one 64-byte row of 32 keys per
+// dimension); the 16-byte columns of row r are XOR-permuted by a function of
+// r's bits 1..3 so that the operand reads below hit every bank group once.
+//
 // Computing the transposed products keeps every operand a 16-byte LDS or
 // register read: the accumulator layout of S^T is directly the B operand of
 // the PV product once the S^T rows (keys) are permuted by swapping index bits
@@ -45,20 +57,47 @@ namespace pa {
 
 namespace {
 
-constexpr int kPW = 8;          // waves per workgroup
-constexpr int kRows = 32 * kPW; // query rows per workgroup
-constexpr int kKT = 32;         // keys per tile
-constexpr int kRing = 3;        // key tiles in flight in registers
-constexpr int kBtStage = 2048;  // table entries staged in LDS (32K tokens at block size 16)
+#ifndef PA_PREFILL_WAVE_ROWS
+#define PA_PREFILL_WAVE_ROWS 32
+#endif
+constexpr int kWR = PA_PREFILL_WAVE_ROWS;  // query rows per wave (halves of 32)
+constexpr int kHalves = kWR / 32;
+constexpr int kRows = 256;                 // query rows per workgroup
+constexpr int kPW = kRows / kWR;           // waves per workgroup
+constexpr int kKT = 32;           // keys per tile
+constexpr int kStages = 4;        // key tiles resident in LDS
+constexpr int kBtStage = 2048;    // table entries staged in LDS (32K tokens at block size 16)
 // The running maximum of a row is moved only when a tile's maximum exceeds
 // it by more than this (log2 units), so probabilities stay below 2^8 and the
 // accumulator rescale is rare; the final division by the row sum cancels
 // whichever reference maximum was used.
 constexpr float kLazy = 8.f;
+// bf16 keeps 8 significant bits of a probability.  Rounding p once is
+// accurate enough for keys that can hold only a small share of their row's
+// final weight; a tile in which some row's largest probability could reach
+// more than this share (judged against the row's sum before the tile, so
+// the first tiles of every row qualify) also multiplies the rounding
+// remainder bf16(p - bf16(p)), which restores about 16 bits.
+constexpr float kSplitShare = 1.f / 16.f;
+// Logit scales are taken as at least this large in magnitude, so that a
+// masked logit (-inf) times the scale stays -inf; every smaller scale gives
+// probabilities that round to those of a zero scale.
+constexpr float kMinScale = 1e-30f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS (lane i's bytes
+// land at lds + 16 i).  The host pass never runs device code, and with the
+// builtin in its view it silently drops the kernels' launch stubs, so it
+// sees an empty body.
+__device__ __forceinline__ void load16_to_lds(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+#endif
+}
 
 template <typename T>
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c);
@@ -83,38 +122,118 @@ __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
   return pack_f16x2(lo, hi);
 }
 
-template <int D>
-struct PrefillSmem {
-  static constexpr int kKStride = D + 8;     // K row stride (elements): 16-byte pad
-  static constexpr int kVStride = kKT + 8;   // V^T row stride (elements)
-  static constexpr int kKElems = kKT * kKStride;
-  static constexpr int kVElems = D * kVStride;
-  static constexpr int kStage = kKElems + kVElems;  // one tile: K rows, then V^T
-  static constexpr int kStages = 3;
-  static constexpr int kBytes = kStages * kStage * 2;
-};
+// The two elements of a packed pair as floats.
+template <typename T>
+__device__ __forceinline__ float lo_value(uint32_t w);
+template <typename T>
+__device__ __forceinline__ float hi_value(uint32_t w);
+template <>
+__device__ __forceinline__ float lo_value<bf16_t>(uint32_t w) {
+  return bf16_lo(w);
+}
+template <>
+__device__ __forceinline__ float hi_value<bf16_t>(uint32_t w) {
+  return bf16_hi(w);
+}
+template <>
+__device__ __forceinline__ float lo_value<f16_t>(uint32_t w) {
+  return f16_lo(w);
+}
+template <>
+__device__ __forceinline__ float hi_value<f16_t>(uint32_t w) {
+  return f16_hi(w);
+}
+
+// acc + both elements of a packed pair: the row sum is taken over the very
+// values the PV product multiplies.
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc);
+template <>
+__device__ __forceinline__ float add_pair<bf16_t>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
+}
+template <>
+__device__ __forceinline__ float add_pair<f16_t>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+}
+
+// Column permutation of the 64-byte LDS rows (four 16-byte columns).  K rows
+// are read by lanes n = 0..31 in the order of keys with index bits 2 and 3
+// swapped, V^T rows in plain order; either way the eight (sixteen) lanes that
+// the LDS serves together then touch eight (sixteen) distinct 16-byte slots.
+__device__ __forceinline__ int kswz(int key) { return (((key >> 1) ^ (key >> 2)) & 1) | (((key >> 3) & 1) << 1); }
+__device__ __forceinline__ int vswz(int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (((d >> 2) & 1) << 1); }
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): at most `vm` vector-memory and `lgkm` LDS/scalar
+// operations of this wave left outstanding.
+constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14); }
+constexpr int kNoWait = 63;
+
+// Wait, then meet the workgroup at a barrier.  The loads straight into LDS
+// count as vector-memory operations; the caller states how many of them may
+// still be in flight.  The empty asm statements keep the compiler from
+// moving memory accesses across.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt(VM, LGKM));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int S>
+using Stage = std::integral_constant<int, S>;
+
+// acc *= alpha, in place.  Written as assembly so that the rescaled values
+// keep the accumulator's registers: as plain code the compiler may give them
+// new ones and then carry two copies of the whole accumulator set around the
+// rarely taken branch (or spill).  The leading no-ops cover the wait states
+// between a matrix product's result and a vector read of it (at most 18 for
+// a 16-pass product), the trailing ones those between a vector write and the
+// next product's accumulator read.
+__device__ __forceinline__ void rescale_acc(f32x16& acc, float alpha) {
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7" : "+v"(acc));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc[j]) : "v"(alpha));
+  asm volatile("s_nop 7" : "+v"(acc));
+}
 
 template <typename T, int D, int B, int G>
-__global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2))) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(kPW / 4, kPW / 4)))
+prefill_kernel(PrefillArgs a) {
+  static_assert(Elem<T>::kBytes == 2, "16-bit pools");
   constexpr int QP = kRows / G;          // positions per workgroup
   constexpr int KSTEPS = D / 16;         // QK contraction steps
   constexpr int DT = D / 32;             // O^T row tiles
   constexpr int NT = kPW * 64;
-  // An FP8 pool's codes are converted to f16 as they are staged in LDS; the
-  // products, the query and the output are f16 then.
-  using CT = typename Src<T>::type;
-  constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
-  constexpr int CE = 16 / Elem<T>::kBytes;  // pool elements per 16-byte chunk
-  static_assert(B % CE == 0, "a chunk of one value row never crosses a block");
-  constexpr int NCHK = kKT * D / CE;     // 16-byte chunks per tile (K, and V)
-  constexpr int CPT = (NCHK + NT - 1) / NT;  // per thread
-  constexpr int RD = kRing;
-  static_assert(RD >= 2, "the prologue stages two tiles from the ring");
-  using S = PrefillSmem<D>;
+  // Share of a row's weight above which a tile also multiplies the rounding
+  // remainders: bf16 probabilities (8 significant bits) need them for large
+  // shares; f16 ones (11 bits) never do, so theirs is 1, which no tile's
+  // test can exceed (0 * p_max > l never holds).  Both types run the same
+  // code, whose register use the compiler then lays out the same way.
+  constexpr float kShare = std::is_same<T, bf16_t>::value ? kSplitShare : 1.f;
+  static_assert(B == kKT || 2 * B == kKT, "a key tile spans one or two blocks");
+  constexpr int kTileBytes = kKT * D * 2;     // K (and V) bytes of one tile
+  constexpr int kStageBytes = 2 * kTileBytes; // K, then V^T
+  constexpr int kPieces = kTileBytes / 1024;  // 1 KB wave loads per K (or V) tile
+  static_assert(2 * kPieces % kPW == 0, "every wave issues the same loads");
+  constexpr int kLoadsPerTile = 2 * kPieces / kPW;  // vector-memory instructions per wave per tile
 
-  __shared__ __align__(16) uint16_t smem[S::kBytes / 2];
-  auto Ks = [&](int st) { return smem + st * S::kStage; };
-  auto Vt = [&](int st) { return smem + st * S::kStage + S::kKElems; };
+  // One array per stage, always addressed with a compile-time stage number:
+  // the compiler can then tell that reads of one stage do not touch the
+  // loads still landing in another, and waits for them only where this code
+  // says so (with a single array it waits for every load in flight before
+  // any LDS read).
+  static_assert(kStages == 4, "four stage arrays below");
+  __shared__ __align__(1024) unsigned char stage0[kStageBytes], stage1[kStageBytes], stage2[kStageBytes],
+      stage3[kStageBytes];
+  auto stage = [&](auto S) -> unsigned char* {
+    constexpr int k = decltype(S)::value % kStages;
+    return k == 0 ? stage0 : k == 1 ? stage1 : k == 2 ? stage2 : stage3;
+  };
+  __shared__ int s_bt[kBtStage];
 
   // Work item.  Workgroup ids are dealt to the 8 XCDs round-robin; remap so
   // that consecutive work items (the query tiles of one sequence and KV head,
@@ -152,32 +271,40 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   const int Hkv = a.cache.num_kv_heads;
   const int Hq = a.num_heads;
 
-  // This lane's query row (column n of the wave's S^T / O^T tiles).
-  const int r = w * 32 + n;
-  const int h = r / QP;
-  const int p = r % QP;
-  const bool row_ok = q0 + p < q_len;
-  const int limit = row_ok ? ctx + q0 + p : -1;
-  const int64_t tok = (int64_t)qbeg + q0 + p;
-  const int hq = g * G + h;
+  // This lane's query rows: column n of the wave's two S^T / O^T halves.
+  bool row_ok[kHalves];
+  int limit[kHalves], hq[kHalves];
+  int64_t tok[kHalves];
   // The smallest causal limit among this wave's rows that exist: a key tile
   // that ends at or below it is visible to all of them, unmasked.
-  int lim_min = row_ok ? limit : 0x7fffffff;
+  int lim_min = 0x7fffffff;
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) {
+    const int r = w * kWR + 32 * hf + n;
+    const int h = r / QP;
+    const int p = r % QP;
+    row_ok[hf] = q0 + p < q_len;
+    limit[hf] = row_ok[hf] ? ctx + q0 + p : -1;
+    tok[hf] = (int64_t)qbeg + q0 + p;
+    hq[hf] = g * G + h;
+    if (row_ok[hf]) lim_min = min(lim_min, limit[hf]);
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, m, 64));
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);  // wave-uniform: scalar branches below
 
   // Q rows as B operands.  A negative scale is moved into Q (negation is
-  // exact), so the logit scale below is never negative and the maximum of
-  // the scaled logits is the scaled maximum.
+  // exact), so the logit scale below is positive and the maximum of the
+  // scaled logits is the scaled maximum.
   const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
-  u32x4 qreg[KSTEPS];
-  {
-    const CT* qrow = reinterpret_cast<const CT*>(a.query) + (tok * Hq + hq) * D;
+  u32x4 qreg[kHalves][KSTEPS];
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) {
+    const T* qrow = reinterpret_cast<const T*>(a.query) + (tok[hf] * Hq + hq[hf]) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
-      qreg[ks] ^= qflip;
+      qreg[hf][ks] = row_ok[hf] ? *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
+      qreg[hf][ks] ^= qflip;
     }
   }
 
@@ -187,7 +314,6 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
   // The table entries this workgroup needs are staged in LDS once (the tile
   // loop would otherwise pay a dependent global read before every K/V load);
   // tables longer than the staging area are read from global memory.
-  __shared__ int s_bt[kBtStage];
   const int nbk = (kend + B - 1) / B;
   const bool staged = nbk <= kBtStage;
   if (staged) {
@@ -197,287 +323,336 @@ __global__ void __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(2
     }
   }
   __syncthreads();
-  // Callers pass pos < kend, so pos / B < nbk; the bound is checked anyway
-  // so that no index outside the staged (validated) entries is ever used.
-  auto block_of = [&](int pos) -> int {
-    const int j = pos / B;
+  // Table entry j as a pool block, -1 past the keys any row sees or outside
+  // the pool (only validated entries are ever used as addresses).
+  auto block_at = [&](int j) -> int {
     if (j >= nbk) return -1;
     if (staged) return s_bt[j];
     const int id = bt[j];
     return (id >= 0 && id < a.cache.num_blocks) ? id : -1;
   };
+  // The one or two blocks of key tile t: fetched one iteration before they
+  // are needed (the LDS read then completes under the barrier's wait instead
+  // of stalling the tile loop), made wave-uniform when used.
+  struct TileBlocks {
+    int b0, b1;
+  };
+  auto fetch_blocks = [&](int t) -> TileBlocks {
+    const int b0 = block_at(t * kKT / B);
+    return {b0, B == kKT ? b0 : block_at(t * kKT / B + 1)};
+  };
+  auto uniform = [](TileBlocks x) -> TileBlocks {
+    return {__builtin_amdgcn_readfirstlane(x.b0), __builtin_amdgcn_readfirstlane(x.b1)};
+  };
 
-  // K piece c of a tile: 16 bytes (dims dch*CE ..) of key `key`, numbered
-  // in the pool's order (the four pieces of a key's 64-byte chunk, then the
-  // tile's keys, then the chunks), so consecutive threads read consecutive
-  // memory.
-  constexpr int KPC = key_chunk<T>() / CE;  // 16-byte pieces per 64-byte chunk
-  auto key_piece = [&](int c, int& key, int& dch) {
-    key = (c / KPC) % kKT;
-    dch = (c / (KPC * kKT)) * KPC + c % KPC;
-  };
-  // Global -> registers for one tile.  K chunks in pool order (coalesced);
-  // V chunks: CE keys of one dimension from the transposed value tile (a
-  // tile of 32 keys never splits such a piece across blocks, since CE
-  // divides the block size).  Keys no row of this workgroup sees (>= kend),
-  // or in blocks outside the pool, read as zeros (their probabilities are
-  // zero; a zero V keeps 0 * V finite).  Up to RD tiles are in flight in
-  // registers at once.
-  u32x4 kregs[RD][CPT], vregs[RD][CPT];
-  auto fetch = [&](u32x4 (&kreg)[CPT], u32x4 (&vreg)[CPT], int t) {
+  // Pool -> LDS for tile t into its stage: 2 * kPieces 1 KB pieces (K, then
+  // V^T), kLoadsPerTile per wave.  Lane i writes bytes 16i .. 16i+15 of its
+  // piece, i.e. row i / 4, stored column i % 4, which holds the pool's
+  // column (i % 4) ^ swizzle(row).  Keys in blocks missing from the pool, or
+  // past the table entries any row needs, load from block 0 (the pool is
+  // never empty): their logits are masked and their V^T columns zeroed
+  // before use (fix_values).
+  auto load_tile = [&](auto S, TileBlocks tb) {
+    const int b0 = tb.b0, b1 = tb.b1;
+    unsigned char* st = stage(S);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      if (NCHK % NT != 0 && c >= NCHK) continue;
-      {
-        int key, dch;
-        key_piece(c, key, dch);
-        const int pos = t * kKT + key;
-        u32x4 x = {0, 0, 0, 0};
-        if (pos < kend) {  // keys >= kend are masked for every row of this tile
-          const int pb = block_of(pos);
-          if (pb >= 0)
-            x = *reinterpret_cast<const u32x4*>(kc + ((int64_t)pb * Hkv + g) * B * D +
-                                                key_tile_offset<T>(pos % B, dch * CE, B));
-        }
-        kreg[i] = x;
-      }
-      {
-        const int kg = c % (kKT / CE), d = c / (kKT / CE);
-        const int pos = t * kKT + kg * CE;
-        u32x4 x = {0, 0, 0, 0};
-        if (pos < kend) {  // keys >= kend are masked for every row of this tile
-          const int pb = block_of(pos);
-          if (pb >= 0) {
-            x = *reinterpret_cast<const u32x4*>(vc + (((int64_t)pb * Hkv + g) * D + d) * B + pos % B);
-            const int nv = kend - pos;  // keys of this piece that some row sees
-            if (nv < CE) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                uint32_t keep;
-                if constexpr (kFp8) {
-                  keep = 0;
-#pragma unroll
-                  for (int b = 0; b < 4; ++b) keep |= (4 * e + b < nv ? 0xffu : 0u) << (8 * b);
-                } else {
-                  keep = 2 * e >= nv ? 0u : (2 * e + 1 >= nv ? 0xffffu : 0xffffffffu);
-                }
-                x[e] &= keep;
-              }
-            }
-          }
-        }
-        vreg[i] = x;
-      }
-    }
-  };
-  // Registers -> LDS (as f16 for an FP8 pool: sixteen codes become two
-  // 16-byte pieces, every E4M3 value being exact in f16).
-  auto put = [&](uint16_t* dst, const u32x4& x) {
-    if constexpr (kFp8) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        lo[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e], 1.0f, false));
-        lo[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e], 1.0f, true));
-        hi[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e + 2], 1.0f, false));
-        hi[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[e + 2], 1.0f, true));
-      }
-      *reinterpret_cast<u32x4*>(dst) = lo;
-      *reinterpret_cast<u32x4*>(dst + 8) = hi;
-    } else {
-      *reinterpret_cast<u32x4*>(dst) = x;
-    }
-  };
-  auto stash = [&](const u32x4 (&kreg)[CPT], const u32x4 (&vreg)[CPT], int st) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      if (NCHK % NT != 0 && c >= NCHK) continue;
-      {
-        int key, dch;
-        key_piece(c, key, dch);
-        put(Ks(st) + key * S::kKStride + dch * CE, kreg[i]);
-      }
-      {
-        const int kg = c % (kKT / CE), d = c / (kKT / CE);
-        put(Vt(st) + d * S::kVStride + kg * CE, vreg[i]);
-      }
+    for (int k = 0; k < kLoadsPerTile; ++k) {
+      // Piece q (wave-uniform): K, chunk q / 2, keys 16 (q % 2) .., or
+      // V^T, dimensions 16 (q - kPieces) ..; selected without a branch, so
+      // that the compiler keeps track of which stage every load writes.
+      const int q = w * kLoadsPerTile + k;
+      const bool is_k = q < kPieces;
+      const int key = 16 * (q % 2) + lane / 4;
+      const int kcol = (lane % 4) ^ kswz(key);
+      const int kblk = (B == kKT || key < B) ? b0 : b1;
+      const int d = 16 * (q - kPieces) + lane / 4;
+      const int vcol = (lane % 4) ^ vswz(d);
+      const int vblk = (B == kKT || 8 * vcol < B) ? b0 : b1;
+      const T* ksrc = kc + ((int64_t)(kblk >= 0 ? kblk : 0) * Hkv + g) * (B * D) + (q / 2) * (B * 32) +
+                      (key % B) * 32 + kcol * 8;
+      const T* vsrc = vc + (((int64_t)(vblk >= 0 ? vblk : 0) * Hkv + g) * D + (is_k ? 0 : d)) * B + (8 * vcol) % B;
+      load16_to_lds(is_k ? ksrc : vsrc, st + q * 1024);
     }
   };
 
-  f32x16 o[DT];
+  // Zero the V^T entries of tile t's keys that no row may see (at or past
+  // kend, or in a missing block), so that 0 * V stays finite whatever the
+  // pool holds there.
+  auto fix_values = [&](auto S, int t, uint32_t gaps) {
+    unsigned char* vt = stage(S) + kTileBytes;
+    const int nvis = kend - t * kKT;  // keys of the tile below kend
+    for (int c = tid; c < D * 4; c += NT) {
+      const int d = c / 4, col = c % 4;
+      const int key0 = 8 * (col ^ vswz(d));
+      u32x4* piece = reinterpret_cast<u32x4*>(vt + d * 64 + col * 16);
+      u32x4 x = *piece;
+      const bool gone = (gaps >> (key0 / 16)) & 1u;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+      for (int e = 0; e < 4; ++e) {
+        const int k = key0 + 2 * e;
+        const uint32_t keep = gone || k >= nvis ? 0u : (k + 1 >= nvis ? 0xffffu : 0xffffffffu);
+        x[e] &= keep;
+      }
+      *piece = x;
+    }
+  };
+
+  f32x16 o[kHalves][DT];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  // FP8: the staged K values are the codes' values; the pool scale joins
-  // the logit scale (and V's the output factor).
-  const float qscale = fabsf(a.scale) * kLog2e * (kFp8 ? a.cache.k_scale : 1.f);
-  // S^T row slot of this lane's A operand, with bits 2 and 3 swapped.
+  for (int hf = 0; hf < kHalves; ++hf)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[hf][dt][j] = 0.f;
+  float m_run[kHalves], l_run[kHalves];
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) {
+    m_run[hf] = -INFINITY;
+    l_run[hf] = 0.f;
+  }
+  const float qscale = fmaxf(fabsf(a.scale) * kLog2e, kMinScale);
+
+  // LDS operand addresses of this lane.  K: key krow (bits 2 and 3 of n
+  // swapped), dimensions 16 ks + 8 hi .. +8 = chunk ks / 2, column
+  // 2 (ks % 2) + hi.  V^T: dimension 32 dt + n, keys 16 ks + 8 hi .. +8 =
+  // column 2 ks + hi.
   const int krow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+  const int koff[2] = {krow * 64 + ((hi ^ kswz(krow)) * 16), krow * 64 + (((2 + hi) ^ kswz(krow)) * 16)};
+  const int voff[2] = {n * 64 + ((hi ^ vswz(n)) * 16), n * 64 + (((2 + hi) ^ vswz(n)) * 16)};
 
-  // S^T = K . Q^T for the tile in stage st.
-  auto scores = [&](int st) {
-    f32x16 acc;
+  // S^T = K . Q^T for the tile in stage st, both halves.
+  auto scores = [&](auto S, f32x16 (&acc)[kHalves]) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-    const uint16_t* krp = Ks(st) + krow * S::kKStride + 8 * hi;
+    for (int hf = 0; hf < kHalves; ++hf)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      acc = mfma32<CT>(*reinterpret_cast<const u32x4*>(krp + 16 * ks), qreg[ks], acc);
-    return acc;
+      for (int j = 0; j < 16; ++j) acc[hf][j] = 0.f;
+    const unsigned char* kb = stage(S);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kb + (ks / 2) * (kKT * 64) + koff[ks % 2]);
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) acc[hf] = mfma32<T>(ka, qreg[hf][ks], acc[hf]);
+    }
   };
 
-  // Online softmax of tile t's scores down the column, in log2 units, into
-  // the P^T operands.  Accumulator j holds key t*32 + 16 (j / 8) + 8 hi +
-  // j % 8 (after the row permutation).  Only tiles that reach past the
-  // wave's smallest limit (the causal diagonal) mask per key.  The running
-  // maximum moves only where the tile exceeds it by more than kLazy; the
-  // probabilities are taken against the moved maximum and the accumulator
-  // rescale (rare) is left to the caller through alpha.
-  u32x4 pb[2], pl[2];
-  // `gaps` bit h (h = 0, 1): keys 16h .. 16h+15 of the tile lie in a block
-  // missing from the pool (table entry outside it).  Such keys hold no
-  // vector, so they are masked like keys past the diagonal, never read as
-  // zeros (a zero key would still add to the row's normaliser).
-  auto softmax = [&](f32x16 sc, int t, bool masked, uint32_t gaps, float& alpha) {
-    float mt = -INFINITY;
-    if (masked) {
-      const int kt0 = t * kKT + 8 * hi;
+  // Masks of tile t's scores: -inf for keys past the row's causal limit or
+  // in a missing block (`gaps` bit h: keys 16h .. 16h+15 of the tile lie in
+  // a block outside the pool; such keys hold no vector, so they are masked,
+  // never read as zeros, which would still add to the row's normaliser).
+  // Accumulator j holds key t*32 + 16 (j / 8) + 8 hi + j % 8 (after the row
+  // permutation).
+  auto mask = [&](f32x16 (&sv)[kHalves], int t, uint32_t gaps) {
+    const int kt0 = t * kKT + 8 * hi;
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = kt0 + 16 * (j >> 3) + (j & 7);
         const bool gone = (gaps >> (j >> 3)) & 1u;
-        sc[j] = key <= limit && !gone ? sc[j] * qscale : -INFINITY;
-        mt = fmaxf(mt, sc[j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sc[j]);
-      mt *= qscale;
-    }
-    mt = max_across_halves(mt);
-    const bool move = mt > m_run + kLazy;
-    const float m_new = move ? mt : m_run;
-    alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
-    m_run = m_new;
-    // A row that has seen no key yet (m_run = -inf) only holds masked
-    // logits: exp2(-inf) = 0 with any finite reference.
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-    float pj[16];
-    if (masked) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(sc[j] - m_ref);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pj[j] = fast_exp2(fmaf(sc[j], qscale, -m_ref));
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ps += pj[j];
-    l_run = l_run * alpha + ps;
-    // P^T as B operands.  f16 keeps 11 significant bits, enough on its own;
-    // bf16 keeps 8, so P is split into a bf16 head and a bf16 remainder and
-    // both are multiplied (the V^T operand is read once for the two).
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = pj[8 * ks + 2 * i], x1 = pj[8 * ks + 2 * i + 1];
-        pb[ks][i] = pack2<CT>(x0, x1);
-        if constexpr (std::is_same<T, bf16_t>::value)
-          pl[ks][i] = pack2<CT>(x0 - bf16_lo(pb[ks][i]), x1 - bf16_hi(pb[ks][i]));
+        sv[hf][j] = key <= limit[hf] && !gone ? sv[hf][j] : -INFINITY;
       }
   };
 
-  // O^T += V^T . P^T for the tile in stage st.
-  auto accumulate = [&](int st) {
+  // Softmax, first part, for a tile's (unscaled) scores: row maxima, the
+  // lazy move of the running maximum and the rescale factor it implies, and
+  // whether the tile needs the rounding remainder.
+  auto phase1 = [&](const f32x16 (&sv)[kHalves], float (&alpha)[kHalves], float (&mref)[kHalves], bool& split_next,
+                    bool& rescale) {
+    bool split = false, moved = false;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vrp = Vt(st) + (32 * dt + n) * S::kVStride + 8 * hi;
+    for (int hf = 0; hf < kHalves; ++hf) {
+      float mt = sv[hf][0];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vrp + 16 * ks);
-        o[dt] = mfma32<CT>(va, pb[ks], o[dt]);
-        if constexpr (std::is_same<T, bf16_t>::value) o[dt] = mfma32<CT>(va, pl[ks], o[dt]);
-      }
+      for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[hf][j]);
+      mt = max_across_halves(mt * qscale);
+      const bool move = mt > m_run[hf] + kLazy;
+      const float m_new = move ? mt : m_run[hf];
+      alpha[hf] = move ? fast_exp2(m_run[hf] - m_new) : 1.f;  // 0 from -inf
+      m_run[hf] = m_new;
+      // A row that has seen no key yet (m_run = -inf) only holds masked
+      // logits: exp2(-inf) = 0 with any finite reference.
+      mref[hf] = m_new == -INFINITY ? 0.f : m_new;
+      l_run[hf] *= alpha[hf];
+      moved = moved || move;
+      // The row's largest probability in this tile against a lower bound of
+      // the row's sum including it: this lane's share of the sum so far plus
+      // that probability.
+      const float pmax = fast_exp2(mt - mref[hf]);
+      split = split || pmax * (1.f - kShare) > kShare * l_run[hf];
+    }
+    split_next = __any(split);
+    rescale = __any(moved);
+  };
+
+  // Softmax, second part: probabilities rounded into the P^T operands, and
+  // their sum.
+  auto phase2 = [&](const f32x16 (&sv)[kHalves], const float (&mref)[kHalves], u32x4 (&pb)[kHalves][2]) {
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 8 * ks + 2 * i;
+          pb[hf][ks][i] = pack2<T>(fast_exp2(fmaf(sv[hf][j], qscale, -mref[hf])),
+                                   fast_exp2(fmaf(sv[hf][j + 1], qscale, -mref[hf])));
+          ps[ks] = add_pair<T>(pb[hf][ks][i], ps[ks]);
+        }
+      l_run[hf] += ps[0] + ps[1];
+    }
+  };
+  // The rounding remainders p - bf16(p) of a tile that needs them (the
+  // probabilities are recomputed: the tile is rare), added to the sum.
+  auto remainders = [&](const f32x16 (&sv)[kHalves], const float (&mref)[kHalves], const u32x4 (&pb)[kHalves][2],
+                        u32x4 (&pl)[kHalves][2]) {
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      float ps = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 8 * ks + 2 * i;
+          const float x0 = fast_exp2(fmaf(sv[hf][j], qscale, -mref[hf]));
+          const float x1 = fast_exp2(fmaf(sv[hf][j + 1], qscale, -mref[hf]));
+          pl[hf][ks][i] = pack2<T>(x0 - lo_value<T>(pb[hf][ks][i]), x1 - hi_value<T>(pb[hf][ks][i]));
+          ps = add_pair<T>(pl[hf][ks][i], ps);
+        }
+      l_run[hf] += ps;
     }
   };
 
-  // Prologue: tiles 0 .. RD-1 load into the register sets, tiles 0 and 1 go
-  // to stages 0 and 1 and their sets are refilled with tiles RD and RD+1.
-#pragma unroll
-  for (int i = 0; i < RD; ++i)
-    if (i < ntiles) fetch(kregs[i], vregs[i], i);
-  stash(kregs[0], vregs[0], 0);
-  if (1 < ntiles) stash(kregs[1], vregs[1], 1);
-  if (RD < ntiles) fetch(kregs[0], vregs[0], RD);
-  if (RD + 1 < ntiles) fetch(kregs[1], vregs[1], RD + 1);
-  __syncthreads();
-  f32x16 sc = scores(0);
-
-  // Iteration t: scores of tile t+1 (stage (t+1) % 3; past the last tile
-  // the stage holds stale data and the result goes unused) with tile t's
-  // softmax, then tile t's PV product (stage t % 3), then tile t+2 from its
-  // register set into stage (t+2) % 3, whose last reader was tile t-1, and
-  // the set refilled with tile t+2+RD.
-  for (int t0 = 0; t0 < ntiles; t0 += RD) {
-#pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      const int t = t0 + i;
-      if (t < ntiles) {
-        // Stage of tile t (a constant when RD is a multiple of 3).
-        const int st0 = RD % 3 == 0 ? i % 3 : t % 3;
-        const int st1 = st0 == 2 ? 0 : st0 + 1;
-        const int st2 = st1 == 2 ? 0 : st1 + 1;
-        float alpha;
-        f32x16 sn;
-        // Wave-uniform: the tile's two 16-key halves each lie in one block.
-        const uint32_t gaps = __builtin_amdgcn_readfirstlane((block_of(t * kKT) < 0 ? 1u : 0u) |
-                                                             (block_of(t * kKT + 16) < 0 ? 2u : 0u));
-        if (t * kKT + kKT - 1 > lim_min || gaps) {
-          sn = scores(st1);
-          softmax(sc, t, true, gaps, alpha);
-        } else {
-          sn = scores(st1);
-          softmax(sc, t, false, 0u, alpha);
-        }
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-        }
-        accumulate(st0);
-        if (t + 2 < ntiles) {
-          stash(kregs[(i + 2) % RD], vregs[(i + 2) % RD], st2);
-          if (t + 2 + RD < ntiles) fetch(kregs[(i + 2) % RD], vregs[(i + 2) % RD], t + 2 + RD);
-        }
-        __syncthreads();
-        sc = sn;
-      }
-    }
-  }
-
-  // Normalise and store this lane's row: accumulator j of tile dt is
-  // dimension 32 dt + 8 (j / 4) + 4 hi + j % 4.
-  const float l_tot = sum_across_halves(l_run);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? (kFp8 ? a.cache.v_scale : 1.f) / l_tot : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (tok * Hq + hq) * D;
+  // O^T += V^T . P^T for the tile in stage st, both halves (P^T: the
+  // rounded probabilities, or their remainders).
+  auto accumulate = [&](auto S, const u32x4 (&pb)[kHalves][2]) {
+    const unsigned char* vb = stage(S) + kTileBytes;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int d = 32 * dt + 8 * j4 + 4 * hi;
-        u32x2 pk;
-        pk[0] = pack2<CT>(o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv);
-        pk[1] = pack2<CT>(o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = pk;
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vb + dt * (32 * 64) + voff[ks]);
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) o[hf][dt] = mfma32<T>(va, pb[hf][ks], o[hf][dt]);
       }
+  };
+
+  auto tile_gaps = [](TileBlocks tb) -> uint32_t { return (tb.b0 < 0 ? 1u : 0u) | (tb.b1 < 0 ? 2u : 0u); };
+  // Tiles that reach past the wave's smallest limit or touch a missing
+  // block are masked (every tile past the last holds only keys >= kend).
+  auto tile_masked = [&](int t, uint32_t gaps) { return t * kKT + kKT - 1 > lim_min || gaps != 0; };
+  // Tiles whose V^T needs fix_values.
+  auto tile_fixed = [&](int t, uint32_t gaps) { return t * kKT + kKT > kend || gaps != 0; };
+
+  // Prologue: tiles 0 .. kStages-2 in flight, tile 0 landed and fixed.
+  const TileBlocks tb0 = uniform(fetch_blocks(0));
+  TileBlocks tb1 = uniform(fetch_blocks(1)), tb2 = uniform(fetch_blocks(2)), tb3;
+  load_tile(Stage<0>(), tb0);
+  load_tile(Stage<1>(), tb1);
+  load_tile(Stage<2>(), tb2);
+  const TileBlocks tb3_raw = fetch_blocks(3);
+  wait_barrier<(kStages - 2) * kLoadsPerTile, kNoWait>();  // tile 0
+  // Two score buffers alternate between iterations (the loop below is
+  // unrolled by four), so neither is ever copied into the other.
+  f32x16 sa[kHalves], sb[kHalves];
+  float alpha[kHalves], mref[kHalves];
+  bool split, rescale;
+  {
+    const uint32_t gaps = tile_gaps(tb0);
+    if (tile_fixed(0, gaps)) fix_values(Stage<0>(), 0, gaps);
+    scores(Stage<0>(), sa);
+    if (tile_masked(0, gaps)) mask(sa, 0, gaps);
+    phase1(sa, alpha, mref, split, rescale);
   }
+  rescale = false;  // the accumulators are still zero
+  wait_barrier<(kStages - 3) * kLoadsPerTile, 0>();  // tile 1, and tile 0's fixed V^T
+  tb3 = uniform(tb3_raw);
+
+  // Iteration t (tile t in stage S = t % kStages, its scores in `cur`): tile
+  // t+kStages-1 starts loading into the stage last read as tile t-1; the
+  // scores of tile t+1 are multiplied into `nxt` while tile t's
+  // probabilities are formed, then tile t's PV product runs while tile
+  // t+1's first softmax part is computed.  At the end, tile t+2 has landed
+  // (waits for the older loads only) and a barrier publishes it.  Past the
+  // last tile the stages hold stale data: tile t+1's keys then lie beyond
+  // every row's limit, its mask removes all of them, and the results go
+  // unused.
+  // tb1, tb2, tb3: the blocks of tiles t+1, t+2, t+3 (uniform).
+  auto iteration = [&](auto S, int t, f32x16 (&cur)[kHalves], f32x16 (&nxt)[kHalves]) {
+    constexpr int st = decltype(S)::value;
+    // At the top of the unrolled loop the compiler merges what it knows of
+    // the loads in flight from two paths and no longer sees which stage they
+    // write, so it would wait for all of them before the first LDS read
+    // below, including the ones issued just before it.  Waiting here, before
+    // this iteration issues any (the only load left is the previous
+    // iteration's, which had that iteration's time to land), costs little
+    // and leaves it nothing to wait for.
+    if constexpr (st == 0) __builtin_amdgcn_s_waitcnt(waitcnt(0, kNoWait));
+    const uint32_t gaps = tile_gaps(tb1);
+    // Tile t+1's V^T is read in the next iteration, after the barrier.  The
+    // condition is the same for every wave (each takes its share).  It is
+    // fixed before this iteration's loads are issued, which the compiler
+    // would otherwise wait for.
+    if (tile_fixed(t + 1, gaps)) fix_values(Stage<st + 1>(), t + 1, gaps);
+    load_tile(Stage<st + kStages - 1>(), tb3);
+    if (rescale) {
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) rescale_acc(o[hf][dt], alpha[hf]);
+    }
+    u32x4 pb[kHalves][2];
+    scores(Stage<st + 1>(), nxt);
+    phase2(cur, mref, pb);
+    accumulate(S, pb);
+    if (split) {
+      u32x4 pl[kHalves][2];
+      remainders(cur, mref, pb, pl);
+      accumulate(S, pl);
+    }
+    if (tile_masked(t + 1, gaps)) mask(nxt, t + 1, gaps);
+    phase1(nxt, alpha, mref, split, rescale);
+    const TileBlocks tb4_raw = fetch_blocks(t + kStages);
+    // Tile t+2 landed (only tile t+3's loads may be outstanding); the LDS
+    // wait also covers fix_values' writes and the block ids just read.
+    wait_barrier<(kStages - 3) * kLoadsPerTile, 0>();
+    tb1 = tb2;
+    tb2 = tb3;
+    tb3 = uniform(tb4_raw);
+  };
+  for (int t = 0; t < ntiles; t += 4) {
+    iteration(Stage<0>(), t, sa, sb);
+    if (t + 1 >= ntiles) break;
+    iteration(Stage<1>(), t + 1, sb, sa);
+    if (t + 2 >= ntiles) break;
+    iteration(Stage<2>(), t + 2, sa, sb);
+    if (t + 3 >= ntiles) break;
+    iteration(Stage<3>(), t + 3, sb, sa);
+  }
+
+  // Normalise and store this lane's rows: accumulator j of tile dt is
+  // dimension 32 dt + 8 (j / 4) + 4 hi + j % 4.
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) {
+    const float l_tot = sum_across_halves(l_run[hf]);
+    if (row_ok[hf]) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (tok[hf] * Hq + hq[hf]) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int d = 32 * dt + 8 * j4 + 4 * hi;
+          u32x2 pk;
+          pk[0] = pack2<T>(o[hf][dt][4 * j4] * inv, o[hf][dt][4 * j4 + 1] * inv);
+          pk[1] = pack2<T>(o[hf][dt][4 * j4 + 2] * inv, o[hf][dt][4 * j4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = pk;
+        }
+    }
+  }
+  // Loads of the tiles past the last may still be in flight: let them land
+  // before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, kNoWait));
 }
 
 template <typename T, int D, int B, int G>
@@ -527,7 +702,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   switch (a.cache.dtype) {
     case DType::kF16: return prefill_d<f16_t>(a, G, stream);
     case DType::kBF16: return prefill_d<bf16_t>(a, G, stream);
-    case DType::kFP8: return prefill_d<fp8_t>(a, G, stream);
+    case DType::kFP8: return launch_prefill_fp8(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,7 +26,7 @@ def _resource_report(src):
         pytest.skip("hipcc not available")
     out = os.path.join(build.BUILD_DIR, os.path.basename(src) + ".resources.o")
     os.makedirs(build.BUILD_DIR, exist_ok=True)
-    cmd = [hipcc, *build.DEVICE_FLAGS, "-I", os.path.join(harness.ROOT, "include"), "-c", src, "-o", out,
+    cmd = [hipcc, *build.device_flags(src), "-I", os.path.join(harness.ROOT, "include"), "-c", src, "-o", out,
            "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -43,7 +43,7 @@ def _resource_report(src):
     return kernels
 
 
-@pytest.mark.parametrize("name", ["decode.hip", "prefill.hip", "cache_ops.hip"])
+@pytest.mark.parametrize("name", ["decode.hip", "prefill.hip", "prefill_fp8.hip", "cache_ops.hip"])
 def test_no_kernel_uses_scratch(name):
     kernels = _resource_report(os.path.join(CSRC, name))
     assert kernels, "no kernels reported"
@@ -57,3 +57,12 @@ def test_benchmark_decode_kernel_keeps_two_waves_per_simd():
     kernels = _resource_report(os.path.join(CSRC, "decode.hip"))
     k = [v for n, v in kernels.items() if "decode_partition_kernelILi8EDF16_Li128ELi16ELi8E" in n]
     assert k and k[0]["Occupancy"] >= 2, k
+
+
+def test_prefill_kernel_keeps_two_waves_per_simd():
+    # The 16-bit prefill kernel runs 8 waves of 32 query rows per workgroup,
+    # two per SIMD, which interleave their matrix and softmax work; its
+    # registers (accumulators included) must fit in the 256 that leaves.
+    kernels = _resource_report(os.path.join(CSRC, "prefill.hip"))
+    k = [v for n, v in kernels.items() if "prefill_kernelINS_6bf16_tELi128ELi32ELi8E" in n]
+    assert k and k[0]["Occupancy"] >= 2 and k[0]["ScratchSize"] == 0, k
