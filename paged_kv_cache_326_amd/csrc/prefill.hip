@@ -235,18 +235,26 @@ prefill_kernel(PrefillArgs a) {
   };
   __shared__ int s_bt[kBtStage];
 
-  // Work item.  Workgroup ids are dealt to the 8 XCDs round-robin; remap so
-  // that consecutive work items (the query tiles of one sequence and KV head,
-  // which read the same K/V) land on the same XCD and share its L2.
+  // Work item: a pair of query tiles of one sequence and KV head, j and
+  // nqt-1-j.  Under the causal mask a tile's key range grows with its
+  // position, so every pair holds about the same work and one round of
+  // workgroups (one per compute unit at the mixed config) ends together;
+  // both tiles read the same K/V.  Workgroup ids are dealt to the 8 XCDs
+  // round-robin; remap so that consecutive pairs (of one sequence and KV
+  // head) land on the same XCD and share its L2.
   const int nqt = a.num_qtiles;
-  const int total = a.num_seqs * a.cache.num_kv_heads * nqt;
+  const int npair = (nqt + 1) / 2;
+  const int total = a.num_seqs * a.cache.num_kv_heads * npair;
   const int per_xcd = (total + 7) / 8;
   const int u = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (u >= total) return;
-  const int qt = u % nqt;
-  const int g = (u / nqt) % a.cache.num_kv_heads;
-  const int s = u / nqt / a.cache.num_kv_heads;
+  const int jp = u % npair;
+  const int g = (u / npair) % a.cache.num_kv_heads;
+  const int s = u / npair / a.cache.num_kv_heads;
 
+  // One query tile: rows q0 .. q0+QP-1 of the chunk (QP positions of the
+  // group's G heads).
+  auto process = [&](const int qt) {
   const int qbeg = a.cu_q_lens[s];
   // Rows stay below the call's token count (the query and output length),
   // whatever the other prefix sums hold.
@@ -352,28 +360,44 @@ prefill_kernel(PrefillArgs a) {
   // past the table entries any row needs, load from block 0 (the pool is
   // never empty): their logits are masked and their V^T columns zeroed
   // before use (fix_values).
+  // Per lane, the byte offset of its 16 bytes inside a block's K (V^T) tile
+  // and which of the tile's two blocks they come from; only the block ids
+  // change from tile to tile.
+  int lane_off[kLoadsPerTile];
+  bool lane_hi[kLoadsPerTile];
+#pragma unroll
+  for (int k = 0; k < kLoadsPerTile; ++k) {
+    // Piece q (wave-uniform): K, chunk q / 2, keys 16 (q % 2) .., or V^T,
+    // dimensions 16 (q - kPieces) ..
+    const int q = w * kLoadsPerTile + k;
+    if (q < kPieces) {
+      const int key = 16 * (q % 2) + lane / 4;
+      const int col = (lane % 4) ^ kswz(key);
+      lane_off[k] = 2 * ((q / 2) * (B * 32) + (key % B) * 32 + col * 8);
+      lane_hi[k] = B != kKT && key >= B;
+    } else {
+      const int d = 16 * (q - kPieces) + lane / 4;
+      const int col = (lane % 4) ^ vswz(d);
+      lane_off[k] = 2 * (d * B + (8 * col) % B);
+      lane_hi[k] = B != kKT && 8 * col >= B;
+    }
+  }
+  const int64_t head_off = (int64_t)g * (B * D) * 2;  // bytes of head g inside a block
   auto load_tile = [&](auto S, TileBlocks tb) {
-    const int b0 = tb.b0, b1 = tb.b1;
     unsigned char* st = stage(S);
+    const int64_t blk_bytes = (int64_t)Hkv * (B * D) * 2;
+    // Missing blocks (-1) read block 0 (the pool is never empty).
+    const int64_t off0 = (tb.b0 >= 0 ? tb.b0 : 0) * blk_bytes + head_off;
+    const int64_t off1 = (tb.b1 >= 0 ? tb.b1 : 0) * blk_bytes + head_off;
 #pragma unroll
     for (int k = 0; k < kLoadsPerTile; ++k) {
-      // Piece q (wave-uniform): K, chunk q / 2, keys 16 (q % 2) .., or
-      // V^T, dimensions 16 (q - kPieces) ..; selected without a branch, so
-      // that the compiler keeps track of which stage every load writes.
       const int q = w * kLoadsPerTile + k;
-      const bool is_k = q < kPieces;
-      const int key = 16 * (q % 2) + lane / 4;
-      const int kcol = (lane % 4) ^ kswz(key);
-      const int kblk = (B == kKT || key < B) ? b0 : b1;
-      const int d = 16 * (q - kPieces) + lane / 4;
-      const int vcol = (lane % 4) ^ vswz(d);
-      const int vblk = (B == kKT || 8 * vcol < B) ? b0 : b1;
-      const T* ksrc = kc + ((int64_t)(kblk >= 0 ? kblk : 0) * Hkv + g) * (B * D) + (q / 2) * (B * 32) +
-                      (key % B) * 32 + kcol * 8;
-      const T* vsrc = vc + (((int64_t)(vblk >= 0 ? vblk : 0) * Hkv + g) * D + (is_k ? 0 : d)) * B + (8 * vcol) % B;
-      load16_to_lds(is_k ? ksrc : vsrc, st + q * 1024);
+      const unsigned char* base =
+          reinterpret_cast<const unsigned char*>(q < kPieces ? kc : vc) + (lane_hi[k] ? off1 : off0);
+      load16_to_lds(base + lane_off[k], st + q * 1024);
     }
   };
+
 
   // Zero the V^T entries of tile t's keys that no row may see (at or past
   // kend, or in a missing block), so that 0 * V stays finite whatever the
@@ -475,10 +499,10 @@ prefill_kernel(PrefillArgs a) {
       l_run[hf] *= alpha[hf];
       moved = moved || move;
       // The row's largest probability in this tile against a lower bound of
-      // the row's sum including it: this lane's share of the sum so far plus
-      // that probability.
+      // the row's sum including it: the sum so far (both lanes of the row)
+      // plus that probability.
       const float pmax = fast_exp2(mt - mref[hf]);
-      split = split || pmax * (1.f - kShare) > kShare * l_run[hf];
+      split = split || pmax * (1.f - kShare) > kShare * sum_across_halves(l_run[hf]);
     }
     split_next = __any(split);
     rescale = __any(moved);
@@ -588,6 +612,7 @@ prefill_kernel(PrefillArgs a) {
     // iteration's, which had that iteration's time to land), costs little
     // and leaves it nothing to wait for.
     if constexpr (st == 0) __builtin_amdgcn_s_waitcnt(waitcnt(0, kNoWait));
+    const TileBlocks tb4_raw = fetch_blocks(t + kStages);  // used after the barrier
     const uint32_t gaps = tile_gaps(tb1);
     // Tile t+1's V^T is read in the next iteration, after the barrier.  The
     // condition is the same for every wave (each takes its share).  It is
@@ -612,7 +637,6 @@ prefill_kernel(PrefillArgs a) {
     }
     if (tile_masked(t + 1, gaps)) mask(nxt, t + 1, gaps);
     phase1(nxt, alpha, mref, split, rescale);
-    const TileBlocks tb4_raw = fetch_blocks(t + kStages);
     // Tile t+2 landed (only tile t+3's loads may be outstanding); the LDS
     // wait also covers fix_values' writes and the block ids just read.
     wait_barrier<(kStages - 3) * kLoadsPerTile, 0>();
@@ -651,13 +675,21 @@ prefill_kernel(PrefillArgs a) {
     }
   }
   // Loads of the tiles past the last may still be in flight: let them land
-  // before the workgroup's LDS is released.
+  // before the workgroup's LDS is reused or released.
   __builtin_amdgcn_s_waitcnt(waitcnt(0, kNoWait));
+  };
+
+  // The longer tile first.
+  process(nqt - 1 - jp);
+  if (jp != nqt - 1 - jp) {
+    __syncthreads();  // every wave is done with the stages and the table
+    process(jp);
+  }
 }
 
 template <typename T, int D, int B, int G>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
-  const int total = a.num_seqs * a.cache.num_kv_heads * a.num_qtiles;
+  const int total = a.num_seqs * a.cache.num_kv_heads * ((a.num_qtiles + 1) / 2);
   const int grid = ((total + 7) / 8) * 8;
   hipLaunchKernelGGL((prefill_kernel<T, D, B, G>), dim3(grid), dim3(kPW * 64), 0, stream, a);
   return hipGetLastError();
