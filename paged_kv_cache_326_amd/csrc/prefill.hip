@@ -65,7 +65,7 @@ constexpr int kHalves = kWR / 32;
 constexpr int kRows = 256;                 // query rows per workgroup
 constexpr int kPW = kRows / kWR;           // waves per workgroup
 constexpr int kKT = 32;           // keys per tile
-constexpr int kStages = 4;        // key tiles resident in LDS
+constexpr int kStages = 6;        // key tiles resident in LDS
 constexpr int kBtStage = 2048;    // table entries staged in LDS (32K tokens at block size 16)
 // The running maximum of a row is moved only when a tile's maximum exceeds
 // it by more than this (log2 units), so probabilities stay below 2^8 and the
@@ -226,12 +226,12 @@ prefill_kernel(PrefillArgs a) {
   // loads still landing in another, and waits for them only where this code
   // says so (with a single array it waits for every load in flight before
   // any LDS read).
-  static_assert(kStages == 4, "four stage arrays below");
+  static_assert(kStages == 6, "six stage arrays below");
   __shared__ __align__(1024) unsigned char stage0[kStageBytes], stage1[kStageBytes], stage2[kStageBytes],
-      stage3[kStageBytes];
+      stage3[kStageBytes], stage4[kStageBytes], stage5[kStageBytes];
   auto stage = [&](auto S) -> unsigned char* {
     constexpr int k = decltype(S)::value % kStages;
-    return k == 0 ? stage0 : k == 1 ? stage1 : k == 2 ? stage2 : stage3;
+    return k == 0 ? stage0 : k == 1 ? stage1 : k == 2 ? stage2 : k == 3 ? stage3 : k == 4 ? stage4 : stage5;
   };
   __shared__ int s_bt[kBtStage];
 
@@ -568,58 +568,41 @@ prefill_kernel(PrefillArgs a) {
   // Tiles whose V^T needs fix_values.
   auto tile_fixed = [&](int t, uint32_t gaps) { return t * kKT + kKT > kend || gaps != 0; };
 
-  // Prologue: tiles 0 .. kStages-2 in flight, tile 0 landed and fixed.
+  // Prologue: tiles 0, 1, 2 landed (and fixed), tile 0's scores and first
+  // softmax part.
+  TileBlocks tb1 = uniform(fetch_blocks(1)), tb2 = uniform(fetch_blocks(2)), tb3 = uniform(fetch_blocks(3)),
+             tb4 = uniform(fetch_blocks(4));
   const TileBlocks tb0 = uniform(fetch_blocks(0));
-  TileBlocks tb1 = uniform(fetch_blocks(1)), tb2 = uniform(fetch_blocks(2)), tb3;
   load_tile(Stage<0>(), tb0);
   load_tile(Stage<1>(), tb1);
   load_tile(Stage<2>(), tb2);
-  const TileBlocks tb3_raw = fetch_blocks(3);
-  wait_barrier<(kStages - 2) * kLoadsPerTile, kNoWait>();  // tile 0
-  // Two score buffers alternate between iterations (the loop below is
-  // unrolled by four), so neither is ever copied into the other.
+  wait_barrier<0, kNoWait>();
+  // Two score buffers alternate between tiles (the loop below handles an
+  // even number of tiles per pass), so neither is ever copied into the other.
   f32x16 sa[kHalves], sb[kHalves];
   float alpha[kHalves], mref[kHalves];
   bool split, rescale;
   {
-    const uint32_t gaps = tile_gaps(tb0);
-    if (tile_fixed(0, gaps)) fix_values(Stage<0>(), 0, gaps);
+    const uint32_t g0 = tile_gaps(tb0), g1 = tile_gaps(tb1), g2 = tile_gaps(tb2);
+    if (tile_fixed(0, g0)) fix_values(Stage<0>(), 0, g0);
+    if (tile_fixed(1, g1)) fix_values(Stage<1>(), 1, g1);
+    if (tile_fixed(2, g2)) fix_values(Stage<2>(), 2, g2);
     scores(Stage<0>(), sa);
-    if (tile_masked(0, gaps)) mask(sa, 0, gaps);
+    if (tile_masked(0, g0)) mask(sa, 0, g0);
     phase1(sa, alpha, mref, split, rescale);
   }
   rescale = false;  // the accumulators are still zero
-  wait_barrier<(kStages - 3) * kLoadsPerTile, 0>();  // tile 1, and tile 0's fixed V^T
-  tb3 = uniform(tb3_raw);
+  wait_barrier<kNoWait, 0>();  // the fixed V^T of tiles 0 .. 2
 
-  // Iteration t (tile t in stage S = t % kStages, its scores in `cur`): tile
-  // t+kStages-1 starts loading into the stage last read as tile t-1; the
-  // scores of tile t+1 are multiplied into `nxt` while tile t's
+  // One tile (t in stage S, its scores in `cur`): the scores of tile t+1
+  // (whose blocks are tb_next) are multiplied into `nxt` while tile t's
   // probabilities are formed, then tile t's PV product runs while tile
-  // t+1's first softmax part is computed.  At the end, tile t+2 has landed
-  // (waits for the older loads only) and a barrier publishes it.  Past the
-  // last tile the stages hold stale data: tile t+1's keys then lie beyond
-  // every row's limit, its mask removes all of them, and the results go
-  // unused.
-  // tb1, tb2, tb3: the blocks of tiles t+1, t+2, t+3 (uniform).
-  auto iteration = [&](auto S, int t, f32x16 (&cur)[kHalves], f32x16 (&nxt)[kHalves]) {
+  // t+1's first softmax part is computed.  Past the last tile the stages
+  // hold stale data: tile t+1's keys then lie beyond every row's limit, its
+  // mask removes all of them, and the results go unused.
+  auto step = [&](auto S, int t, f32x16 (&cur)[kHalves], f32x16 (&nxt)[kHalves], TileBlocks tb_next) {
     constexpr int st = decltype(S)::value;
-    // At the top of the unrolled loop the compiler merges what it knows of
-    // the loads in flight from two paths and no longer sees which stage they
-    // write, so it would wait for all of them before the first LDS read
-    // below, including the ones issued just before it.  Waiting here, before
-    // this iteration issues any (the only load left is the previous
-    // iteration's, which had that iteration's time to land), costs little
-    // and leaves it nothing to wait for.
-    if constexpr (st == 0) __builtin_amdgcn_s_waitcnt(waitcnt(0, kNoWait));
-    const TileBlocks tb4_raw = fetch_blocks(t + kStages);  // used after the barrier
-    const uint32_t gaps = tile_gaps(tb1);
-    // Tile t+1's V^T is read in the next iteration, after the barrier.  The
-    // condition is the same for every wave (each takes its share).  It is
-    // fixed before this iteration's loads are issued, which the compiler
-    // would otherwise wait for.
-    if (tile_fixed(t + 1, gaps)) fix_values(Stage<st + 1>(), t + 1, gaps);
-    load_tile(Stage<st + kStages - 1>(), tb3);
+    const uint32_t gaps = tile_gaps(tb_next);
     if (rescale) {
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf)
@@ -637,21 +620,41 @@ prefill_kernel(PrefillArgs a) {
     }
     if (tile_masked(t + 1, gaps)) mask(nxt, t + 1, gaps);
     phase1(nxt, alpha, mref, split, rescale);
-    // Tile t+2 landed (only tile t+3's loads may be outstanding); the LDS
-    // wait also covers fix_values' writes and the block ids just read.
-    wait_barrier<(kStages - 3) * kLoadsPerTile, 0>();
-    tb1 = tb2;
-    tb2 = tb3;
-    tb3 = uniform(tb4_raw);
   };
-  for (int t = 0; t < ntiles; t += 4) {
-    iteration(Stage<0>(), t, sa, sb);
-    if (t + 1 >= ntiles) break;
-    iteration(Stage<1>(), t + 1, sb, sa);
+
+  // A pass covers tiles t and t+1 (in stages S and S+1) between two
+  // barriers: tiles t+3 and t+4 start loading (into the stages last read as
+  // tiles t-3 and t-2), then the two tiles run; at the end every load of the
+  // pass has landed (it had the two tiles' time), tiles whose values need
+  // it are fixed, and a barrier publishes them.  tb1 .. tb4: the blocks of
+  // tiles t+1 .. t+4 (uniform).
+  auto pass = [&](auto S, int t) {
+    constexpr int st = decltype(S)::value;
+    load_tile(Stage<st + 3>(), tb3);
+    load_tile(Stage<st + 4>(), tb4);
+    const TileBlocks tb5_raw = fetch_blocks(t + 5), tb6_raw = fetch_blocks(t + 6);  // used after the barrier
+    step(S, t, sa, sb, tb1);
+    if (t + 1 < ntiles) step(Stage<st + 1>(), t + 1, sb, sa, tb2);
+    const uint32_t g3 = tile_gaps(tb3), g4 = tile_gaps(tb4);
+    const bool fix3 = tile_fixed(t + 3, g3), fix4 = tile_fixed(t + 4, g4);
+    if (fix3 || fix4) {
+      // Every wave's loads must have landed before any wave fixes them.
+      wait_barrier<0, 0>();
+      if (fix3) fix_values(Stage<st + 3>(), t + 3, g3);
+      if (fix4) fix_values(Stage<st + 4>(), t + 4, g4);
+    }
+    wait_barrier<0, 0>();
+    tb1 = tb3;
+    tb2 = tb4;
+    tb3 = uniform(tb5_raw);
+    tb4 = uniform(tb6_raw);
+  };
+  for (int t = 0; t < ntiles; t += 6) {
+    pass(Stage<0>(), t);
     if (t + 2 >= ntiles) break;
-    iteration(Stage<2>(), t + 2, sa, sb);
-    if (t + 3 >= ntiles) break;
-    iteration(Stage<3>(), t + 3, sb, sa);
+    pass(Stage<2>(), t + 2);
+    if (t + 4 >= ntiles) break;
+    pass(Stage<4>(), t + 4);
   }
 
   // Normalise and store this lane's rows: accumulator j of tile dt is
