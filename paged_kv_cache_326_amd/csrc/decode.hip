@@ -255,6 +255,57 @@ decode_partition_kernel(DecodeArgs a) {
     if (wi < 0 || wi >= a.num_seqs * a.num_partitions) return;  // not a unit of this call
     s = wi / a.num_partitions;
     part = wi % a.num_partitions;
+  } else if (a.device_plan) {
+    // The plan computed on the device (a batch of at most 64 sequences, one
+    // length per lane; every wave computes the same): workgroup i serves KV
+    // head i % H_kv of the unit of rank i / H_kv in the order full
+    // partitions first (partition-major), then each sequence's last, partial
+    // one by decreasing size in eighths of a partition (and the partition 0
+    // of empty sequences, which writes their zeros).  Ranks past the last
+    // unit exit at once: they come last in the grid, where they cost
+    // nothing.
+    const int lane = threadIdx.x & 63;
+    int Ls = lane < a.num_seqs ? a.seq_lens[lane] : -1;
+    Ls = Ls < 0 ? (lane < a.num_seqs ? 0 : -1) : (Ls > a.max_seq_len ? a.max_seq_len : Ls);
+    const int full = Ls > 0 ? Ls / a.partition : 0;
+    const int rem = Ls >= 0 ? Ls - full * a.partition : 0;
+    const bool partial = Ls == 0 || rem > 0;
+    int u = (int)(blockIdx.x / a.cache.num_kv_heads);
+    g = blockIdx.x % a.cache.num_kv_heads;
+    s = -1;
+    part = 0;
+    // The unit of rank u among the lanes set in m: the u-th set lane.
+    auto pick = [&](uint64_t m) -> int {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint64_t hit = __ballot(((m >> lane) & 1u) && below == u);
+      return hit ? (int)__builtin_ctzll(hit) : -1;
+    };
+    for (int q = 0;; ++q) {
+      const uint64_t m = __ballot(full > q);
+      if (!m) break;
+      const int c = __builtin_popcountll(m);
+      if (u < c) {
+        s = pick(m);
+        part = q;
+        break;
+      }
+      u -= c;
+    }
+    if (s < 0) {
+      for (int b = 7; b >= 0; --b) {
+        const uint64_t m = __ballot(partial && (rem * 8) / a.partition == b);
+        const int c = __builtin_popcountll(m);
+        if (u < c) {
+          s = pick(m);
+          part = __builtin_amdgcn_readlane(full, s);
+          break;
+        }
+        u -= c;
+      }
+    }
+    s = __builtin_amdgcn_readfirstlane(s);
+    part = __builtin_amdgcn_readfirstlane(part);
+    if (s < 0) return;  // past the last unit of this call
   } else {
     const int sg = blockIdx.x % (a.num_seqs * a.cache.num_kv_heads);
     part = a.num_partitions - 1 - (int)(blockIdx.x / (a.num_seqs * a.cache.num_kv_heads));
@@ -683,9 +734,9 @@ __global__ void __launch_bounds__(G * D / 4) decode_reduce_kernel(DecodeArgs a) 
   int L = a.seq_lens[s];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   // Without a plan every partition wrote its partials or an m = -inf marker,
-  // so the loads need not wait for seq_len; with one, only the sequence's
-  // own partitions ran.
-  const int np = a.work ? (L + a.partition - 1) / a.partition : a.num_partitions;
+  // so the loads need not wait for seq_len; with one (from the host or made
+  // on the device), only the sequence's own partitions ran.
+  const int np = a.work || a.device_plan ? (L + a.partition - 1) / a.partition : a.num_partitions;
   const f32x4 v = merge_partials<D>(a, s, hq, d, np);
   if (L <= a.partition) return;  // written directly by the partition kernel
   store4<T>(reinterpret_cast<T*>(a.out) + ((int64_t)s * a.num_heads + hq) * D + d, v);

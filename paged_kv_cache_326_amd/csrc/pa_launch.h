@@ -41,6 +41,11 @@ struct DecodeArgs {
   // num_work launched units (else the grid covers every partition).
   const int32_t* work;
   int32_t num_work;
+  // Without a plan, for batches of at most kDevicePlanSeqs sequences: each
+  // workgroup reads every length and takes the unit of its rank in the
+  // longest-first order itself (see decode.hip); the merge then reads only
+  // the partitions a sequence has.
+  int32_t device_plan;
   float* ws_m;            // [num_seqs][num_heads][num_partitions]
   float* ws_l;            // same
   float* ws_o;            // [num_seqs][num_heads][num_partitions][head_dim]
@@ -60,6 +65,7 @@ struct PrefillArgs {
 };
 
 constexpr int kMaxPartition = 4096;
+constexpr int kDevicePlanSeqs = 64;  // one length per lane of a wave
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                                const int32_t* cu_q_lens, int32_t num_seqs, int32_t block_size,
