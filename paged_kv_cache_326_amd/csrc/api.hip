@@ -273,7 +273,10 @@ static pa_status decode_run(const pa_decode_args* d, hipStream_t stream) {
   a.num_partitions = max_seq_len > 0 ? ceil_div(max_seq_len, p) : 1;
   a.work = d->work;
   a.num_work = d->work ? d->num_work : 0;
-  a.device_plan = !d->work && a.num_partitions > 1 && num_seqs <= pa::kDevicePlanSeqs;
+  // With at most two partitions per sequence the full grid's order (last
+  // partitions first) is already longest-first; the order made on the device
+  // pays off from three on.
+  a.device_plan = !d->work && a.num_partitions > 2 && num_seqs <= pa::kDevicePlanSeqs;
   // 8-wave workgroups (one per compute unit) when the workgroups fit in one
   // round of the chip, else 4-wave ones (three per compute unit).
   const int64_t units = d->work ? (int64_t)d->num_work : (int64_t)num_seqs * a.num_partitions;

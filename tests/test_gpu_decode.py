@@ -269,7 +269,7 @@ def test_decode_device_order_covers_every_partition(num_seqs):
     # one token past one, single-partition sequences, several full
     # partitions, and the eighths the partial units are ordered by.
     rng = np.random.default_rng(num_seqs)
-    P = 64
+    P = 32
     special = [0, 1, P - 1, P, P + 1, 2 * P, 2 * P + 1, 5 * P, 5 * P + 7, 8, P // 8, P // 8 + 1, 0, 3 * P - 1]
     lens = special + list(rng.integers(1, 6 * P, num_seqs - len(special)))
     w = synth.custom(seed=300 + num_seqs, dtype="f16", num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
