@@ -433,6 +433,41 @@ def prefill_only(steps: int, warmup: int, copies_n: int, fp8: bool):
     }
 
 
+def fp8_decode_only(steps: int, warmup: int, copies_n: int, partition: int = 0):
+    """The benchmark layer's decode over FP8 (E4M3) pools alone (the same
+    float16 rows quantised by the library's scatter, per-tensor scales), for
+    counter collection on the FP8 partition and merge kernels: one JSON line
+    with its mean call time and HBM rate on the halved bytes."""
+    import torch
+    from paged_kv_cache_326_amd import pa, synth
+    from tests import harness
+
+    scales = (0.0173, 0.0291)
+    w = synth.config(2, poison_unused=False)
+    P = partition or pa.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, w.max_seq_len, w.block_size)
+    cs = _copies(w, copies_n)
+    runs = []
+    for c in cs:
+        kc8, vc8 = harness.fp8_pool_gpu(c, scales)
+        runs.append((c, kc8, vc8, pa.decode_workspace(c.query, kc8, w.max_seq_len, P)))
+        c.key_cache = c.value_cache = None
+    torch.cuda.empty_cache()
+
+    def run(i):
+        c, kc8, vc8, ws = runs[i % len(runs)]
+        pa.pa_decode(c.out, c.query, kc8, vc8, c.block_tables, c.seq_lens, w.scale, w.max_seq_len, workspace=ws,
+                     partition_size=P, scales=scales)
+
+    for i in range(warmup):
+        run(i)
+    t = _burst_us(run, iters=steps)
+    nb = algorithmic_decode_bytes(w, kv_elem_bytes=1)
+    return {
+        "workload": "fp8_e4m3_" + synth.CONFIG_NAMES[2], "partition": P, "decode_us": round(t, 2),
+        "algorithmic_bytes": nb, "frac_of_hbm_peak": round(nb / t / 1e3 / HBM_PEAK_GBS, 4), "steps": steps,
+    }
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """Time the oracle (as it stands) on this host: scatter + decode of the
     whole batch, repeated until `budget_s` has elapsed (at least once)."""
@@ -524,6 +559,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
     ap.add_argument("--prefill", choices=("bf16", "fp8"), default=None,
                     help="time only the mixed config's chunked prefill (for counter collection)")
+    ap.add_argument("--fp8-decode", action="store_true",
+                    help="time only the benchmark layer's decode over FP8 pools (for counter collection)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="instead: time a plain streaming read of the benchmark layer's bytes at several launch shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -566,6 +603,9 @@ def main():
 
     if args.prefill:
         print(json.dumps(prefill_only(args.steps, args.warmup, args.copies, args.prefill == "fp8")), flush=True)
+        return
+    if args.fp8_decode:
+        print(json.dumps(fp8_decode_only(args.steps, args.warmup, args.copies, args.partition)), flush=True)
         return
     if args.stream_ceiling:
         nb = algorithmic_decode_bytes(synth.config(2, poison_unused=False))
