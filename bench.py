@@ -258,10 +258,12 @@ def secondary(copies_n: int):
     }
     del cs, gps, gds, wsd
     torch.cuda.empty_cache()
-    # Indirection: identity vs permuted layout of the benchmark layer.
+    # Indirection: the benchmark layer's random block layout against fixed
+    # ones (contiguous runs, runs with staggered starts, interleaved).
     w = synth.config(2, poison_unused=False)
     out = {}
-    for name, ww in (("permuted", w), ("identity", synth.identity_tables(w))):
+    for name in ("permuted", "identity", "rotated", "interleaved"):
+        ww = w if name == "permuted" else synth.layout_tables(w, name)
         cs = _copies(ww, copies_n)
         ws = [pa.decode_workspace(c.query, c.key_cache, ww.max_seq_len) for c in cs]
         out[name] = _burst_us(lambda i: cs[i % len(cs)].decode(workspace=ws[i % len(cs)]))
@@ -269,6 +271,7 @@ def secondary(copies_n: int):
         torch.cuda.empty_cache()
     res["block_table_indirection"] = {
         "permuted_us": round(out["permuted"], 2), "identity_us": round(out["identity"], 2),
+        "rotated_us": round(out["rotated"], 2), "interleaved_us": round(out["interleaved"], 2),
         "overhead_pct": round(100.0 * (out["permuted"] / out["identity"] - 1.0), 2),
     }
     # The benchmark layer over an FP8 (E4M3) pool: the same float16 rows
@@ -555,6 +558,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="decode partition length (0 = automatic)")
     ap.add_argument("--copies", type=int, default=3, help="rotated pool copies")
     ap.add_argument("--identity-tables", action="store_true", help="unpermuted block layout (indirection overhead)")
+    ap.add_argument("--layout", choices=("permuted", "identity", "rotated", "interleaved"), default="permuted",
+                    help="block layout of the pool (permuted: the workload's random one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configs' measurements")
     ap.add_argument("--prefill", choices=("bf16", "fp8"), default=None,
@@ -614,7 +619,9 @@ def main():
 
     w = synth.config(args.config, poison_unused=False)
     if args.identity_tables:
-        w = synth.identity_tables(w)
+        args.layout = "identity"
+    if args.layout != "permuted":
+        w = synth.layout_tables(w, args.layout)
     P = args.partition or pa.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, w.max_seq_len, w.block_size)
     copies = [harness.GpuWorkload(w)]
     for _ in range(args.copies - 1):
@@ -697,7 +704,7 @@ def main():
             "head_dim": w.head_dim,
             "block_size": w.block_size,
             "num_blocks": w.num_blocks,
-            "block_tables": "identity" if args.identity_tables else "random permutation",
+            "block_tables": "random permutation" if args.layout == "permuted" else args.layout,
             "partition": P,
             "pool_copies": len(copies),
         },
@@ -709,7 +716,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic() if args.config == 2 and not args.identity_tables else None,
+            "traffic": measured_traffic() if args.config == 2 and args.layout == "permuted" else None,
             "algorithmic_bytes": nbytes_kernel,
             "kernel_us_mean": float(part_ms.mean()) * 1e3,
             "kernel_us_median": float(np.median(part_ms)) * 1e3,
@@ -723,7 +730,7 @@ def main():
         },
         "attended_kv_tokens_per_s_decode": attended / dec_avg_s,
     }
-    if not args.no_secondary and args.config == 2 and not args.identity_tables:
+    if not args.no_secondary and args.config == 2 and args.layout == "permuted":
         del copies, ws
         torch.cuda.empty_cache()
         rec["secondary"] = secondary(args.copies)

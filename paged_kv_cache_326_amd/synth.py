@@ -413,17 +413,33 @@ def custom(
     )
 
 
-def identity_tables(w: Workload) -> Workload:
-    """The same logical content with each sequence's blocks laid out
-    contiguously in pool order (sequence 0's blocks first): the unpermuted
-    layout against which indirection overhead is measured."""
+def layout_tables(w: Workload, kind: str = "identity") -> Workload:
+    """The same logical content with the sequences' blocks placed in the
+    pool in a fixed pattern instead of the generator's random permutation
+    (the blocks no sequence uses follow, in their old order):
+
+    * ``identity``: each sequence's blocks contiguous, sequence 0 first;
+    * ``rotated``: contiguous runs as in ``identity``, but sequence s's run
+      starts at its block (37 s) mod n_s and wraps around;
+    * ``interleaved``: block i of every sequence before block i + 1 of any
+      (round-robin over the sequences that still have a block i).
+
+    Used to measure what the block layout costs the decode."""
     S, MB = w.block_tables.shape
     B = w.block_size
     nblk = [_ceil_div(L, B) for L in w.seq_lens]
     used = int(sum(nblk))
     if w.refcounts.max() > 1:
-        raise ValueError("identity layout needs private blocks")
-    order = np.concatenate([w.block_tables[s, : nblk[s]] for s in range(S)]) if S else np.zeros(0, np.int32)
+        raise ValueError("a fixed layout needs private blocks")
+    if kind == "identity":
+        order = [w.block_tables[s, i] for s in range(S) for i in range(nblk[s])]
+    elif kind == "rotated":
+        order = [w.block_tables[s, (i + 37 * s) % nblk[s]] for s in range(S) for i in range(nblk[s])]
+    elif kind == "interleaved":
+        order = [w.block_tables[s, i] for i in range(max(nblk, default=0)) for s in range(S) if i < nblk[s]]
+    else:
+        raise ValueError(f"unknown layout {kind!r}")
+    order = np.asarray(order, np.int32)
     rest = np.setdiff1d(np.arange(w.num_blocks, dtype=np.int32), order)
     new_of_old = np.empty(w.num_blocks, np.int32)
     new_of_old[order] = np.arange(used, dtype=np.int32)
@@ -441,3 +457,9 @@ def identity_tables(w: Workload) -> Workload:
         value_cache=np.ascontiguousarray(w.value_cache[perm]),
         refcounts=w.refcounts[perm].copy(),
     )
+
+
+def identity_tables(w: Workload) -> Workload:
+    """Each sequence's blocks contiguous in pool order (sequence 0 first):
+    the unpermuted layout against which indirection overhead is measured."""
+    return layout_tables(w, "identity")
