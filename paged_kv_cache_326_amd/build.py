@@ -87,5 +87,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+HOST_SANITIZED_LIB = os.path.join(BUILD_DIR, "libpa_host_sanitized.so")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The library's host C++ alone (block manager, scheduler) as a shared
+    library instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts), for running their CPU tests under the sanitizers:
+    pa.py loads it when PA_LIB names it, in a process that preloads
+    libasan.  No device code is involved."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+    cmd = [shutil.which("g++") or "g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+           *srcs, "-o", HOST_SANITIZED_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed on the host sources:\n{r.stdout}\n{r.stderr}")
+    return HOST_SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -15,7 +15,9 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIB may name another build of the library: the sanitizer run of the
+# host C++ loads one that holds only the block manager and the scheduler.
+_LIB_PATH = os.environ.get("PA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 # An FP8 (OCP E4M3) pool is a uint8 (or float8_e4m3fn) tensor of codes; its
@@ -35,7 +37,11 @@ PA_ERR_EXISTS = 8
 class PaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {_STATUS.get(status, status)} ({lib().pa_status_string(status).decode()})")
+        try:
+            detail = lib().pa_status_string(status).decode()
+        except RuntimeError:  # a partial build (PA_LIB) without pa_status_string
+            detail = "no description in this build"
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({detail})")
 
 
 class pa_kv_cache(ctypes.Structure):
@@ -79,6 +85,32 @@ class pa_decode_args(ctypes.Structure):
 
 
 _lib = None
+
+
+class _Absent:
+    """Stands for an entry point that a partial build (PA_LIB) lacks: its
+    signature may be declared, a call raises."""
+
+    def __init__(self, name: str):
+        self.__dict__["_name"] = name
+
+    def __call__(self, *args):
+        raise RuntimeError(f"{self._name} is not in {_LIB_PATH}")
+
+
+class _Partial:
+    """A library loaded through PA_LIB that may lack some entry points."""
+
+    def __init__(self, L: ctypes.CDLL):
+        self._L = L
+
+    def __getattr__(self, name: str):
+        try:
+            f = getattr(self._L, name)
+        except AttributeError:
+            f = _Absent(name)
+        setattr(self, name, f)
+        return f
 
 EXPORTS = (
     "pa_slot_mapping",
@@ -143,6 +175,8 @@ def lib() -> ctypes.CDLL:
             f"{_LIB_PATH} is not built; run `python -m paged_kv_cache_326_amd.build` (hipcc, gfx950)"
         )
     L = ctypes.CDLL(_LIB_PATH)
+    if os.environ.get("PA_LIB"):
+        L = _Partial(L)
     vp, i32, i64p, i32p, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     cache_p = ctypes.POINTER(pa_kv_cache)
     L.pa_slot_mapping.argtypes = [i32p, i32, i32p, i32p, i32, i32, i64p, i32, vp]
@@ -315,6 +349,97 @@ def kv_cache(key_cache: torch.Tensor, value_cache: torch.Tensor, scales=None) ->
     return pa_kv_cache(key_cache.data_ptr(), value_cache.data_ptr(), NB, H, NC * KC, B, _DTYPE[key_cache.dtype], ks, vs)
 
 
+def debug_enabled() -> bool:
+    """PA_DEBUG=1: before each launch the binding copies the device-resident
+    contents the kernels trust (block tables, lengths, slots, chunk offsets,
+    block lists) to the host and checks them, raising ValueError instead of
+    launching.  The copies wait for the stream: a debugging aid, not for
+    timed runs.  Without it those contents are the caller's contract (the
+    kernels skip block ids outside the pool and negative slots, and clamp
+    lengths, but compute nothing meaningful from them)."""
+    return os.environ.get("PA_DEBUG", "0") not in ("", "0")
+
+
+def _host(t):
+    import numpy as np
+
+    return t.detach().cpu().numpy() if torch.is_tensor(t) else np.asarray(t)
+
+
+def debug_check_tables(block_tables, seq_lens, num_blocks: int, block_size: int, max_seq_len: int, what: str):
+    """Every length in [0, max_seq_len] and within its table row; every
+    block id a sequence reads (its first ceil(L / block_size) entries) in
+    [0, num_blocks)."""
+    import numpy as np
+
+    bt, L = _host(block_tables), _host(seq_lens).astype(np.int64)
+    bad = np.nonzero((L < 0) | (L > max_seq_len))[0]
+    if bad.size:
+        raise ValueError(f"{what}: seq_lens[{bad[0]}] = {L[bad[0]]} outside [0, max_seq_len = {max_seq_len}]")
+    need = -(-L // block_size)
+    bad = np.nonzero(need > bt.shape[1])[0]
+    if bad.size:
+        raise ValueError(f"{what}: sequence {bad[0]} needs {need[bad[0]]} blocks, its table row holds {bt.shape[1]}")
+    used = np.arange(bt.shape[1])[None, :] < need[:, None]
+    s, i = np.nonzero(used & ((bt < 0) | (bt >= num_blocks)))
+    if s.size:
+        raise ValueError(f"{what}: block_tables[{s[0]}][{i[0]}] = {bt[s[0], i[0]]} outside the pool [0, {num_blocks})")
+
+
+def debug_check_slots(slot_mapping, num_tokens: int, num_blocks: int, block_size: int, what: str):
+    """The first num_tokens slots: negative (skip) or in the pool, and no
+    slot written twice."""
+    import numpy as np
+
+    sl = _host(slot_mapping)[:num_tokens].astype(np.int64)
+    bad = np.nonzero(sl >= (np.int64(num_blocks) * block_size))[0]
+    if bad.size:
+        raise ValueError(f"{what}: slot_mapping[{bad[0]}] = {sl[bad[0]]} beyond the pool ({num_blocks} x {block_size})")
+    live = np.sort(sl[sl >= 0])
+    dup = np.nonzero(live[1:] == live[:-1])[0]
+    if dup.size:
+        raise ValueError(f"{what}: slot {live[dup[0]]} is written by two tokens")
+
+
+def debug_check_chunks(cu_q_lens, seq_lens, max_q_len: int, num_tokens: int, what: str):
+    """Chunk offsets start at 0, never decrease and stay within the token
+    rows; every chunk fits max_q_len and its sequence's length."""
+    import numpy as np
+
+    cu, L = _host(cu_q_lens).astype(np.int64), _host(seq_lens).astype(np.int64)
+    q = np.diff(cu)
+    if cu.size == 0 or cu[0] != 0:
+        raise ValueError(f"{what}: cu_q_lens must start at 0")
+    bad = np.nonzero(q < 0)[0]
+    if bad.size:
+        raise ValueError(f"{what}: cu_q_lens decreases at sequence {bad[0]}")
+    if cu[-1] > num_tokens:
+        raise ValueError(f"{what}: cu_q_lens ends at {cu[-1]}, beyond the {num_tokens} token rows")
+    bad = np.nonzero(q > max_q_len)[0]
+    if bad.size:
+        raise ValueError(f"{what}: chunk {bad[0]} has {q[bad[0]]} tokens, more than max_q_len = {max_q_len}")
+    bad = np.nonzero(q > L)[0]
+    if bad.size:
+        raise ValueError(f"{what}: chunk {bad[0]} has {q[bad[0]]} tokens but seq_lens[{bad[0]}] = {L[bad[0]]}")
+
+
+def debug_check_blocks(ids, num_blocks: int, what: str, distinct: bool = False, other=None):
+    """Block ids in [0, num_blocks); with ``distinct`` none twice, and none
+    also in ``other`` (a copy's sources)."""
+    import numpy as np
+
+    b = _host(ids).astype(np.int64).ravel()
+    bad = np.nonzero((b < 0) | (b >= num_blocks))[0]
+    if bad.size:
+        raise ValueError(f"{what}: block id {b[bad[0]]} outside the pool [0, {num_blocks})")
+    if distinct:
+        sb = np.sort(b)
+        if (sb[1:] == sb[:-1]).any():
+            raise ValueError(f"{what}: a destination block appears twice")
+        if other is not None and np.intersect1d(b, _host(other)).size:
+            raise ValueError(f"{what}: a block is both a source and a destination")
+
+
 def _check(status: int, what: str):
     if status != 0:
         raise PaError(status, what)
@@ -330,6 +455,10 @@ def pa_slot_mapping(block_tables, seq_lens, cu_q_lens, block_size: int, slot_map
     if slot_mapping is None:
         slot_mapping = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
     _need(slot_mapping, "slot_mapping", torch.int64)
+    if debug_enabled():
+        MB = block_tables.shape[1]
+        debug_check_tables(block_tables, seq_lens, 2**31 - 1, block_size, MB * block_size, "pa_slot_mapping")
+        debug_check_chunks(cu_q_lens, seq_lens, MB * block_size, num_tokens, "pa_slot_mapping")
     st = lib().pa_slot_mapping(block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), cu_q_lens.data_ptr(),
                                S, block_size, slot_mapping.data_ptr(), num_tokens, _stream(stream))
     _check(st, "pa_slot_mapping")
@@ -344,6 +473,8 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, strea
     T = key.shape[0]
     if key.shape != (T, c.num_kv_heads, c.head_dim) or value.shape != key.shape or slot_mapping.shape[0] < T:
         raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] with one slot per token")
+    if debug_enabled():
+        debug_check_slots(slot_mapping, T, c.num_blocks, c.block_size, "pa_reshape_and_cache")
     st = lib().pa_reshape_and_cache(ctypes.byref(c), key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), T, _stream(stream))
     _check(st, "pa_reshape_and_cache")
 
@@ -363,6 +494,10 @@ def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_
     if slot_mapping is None:
         slot_mapping = torch.empty(T, dtype=torch.int64, device=key.device)
     _need(slot_mapping, "slot_mapping", torch.int64)
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, block_tables.shape[1] * c.block_size,
+                           "pa_append_kv")
+        debug_check_chunks(cu_q_lens, seq_lens, int(max_q_len), T, "pa_append_kv")
     st = lib().pa_append_kv(ctypes.byref(c), key.data_ptr(), value.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
                             seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, int(max_q_len), slot_mapping.data_ptr(), T,
                             _stream(stream))
@@ -402,6 +537,8 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, seq_lens, scale:
         workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode")
     args = (ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
             seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(), ws_bytes, int(partition_size))
     if stage:
@@ -430,6 +567,8 @@ def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, seq_lens
     S, Hq, D = query.shape
     if out.shape != query.shape or D != c.head_dim or block_tables.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("shape mismatch between query/out/block_tables/seq_lens and the cache")
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode_noalloc")
     st = lib().pa_decode_noalloc(ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(),
                                  block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
                                  int(partition_size), _stream(stream))
@@ -462,6 +601,8 @@ def pa_decode_timed(out, query, key_cache, value_cache, block_tables, seq_lens, 
     if workspace is None:
         workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
     _need(workspace, "workspace")
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode_timed")
     st = lib().pa_decode_timed(ctypes.byref(c), out.data_ptr(), query.data_ptr(), block_tables.data_ptr(),
                                block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), int(partition_size),
@@ -495,6 +636,8 @@ def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, blo
     _need(workspace, "workspace")
     ev0 = None if kernel_start is None else _event_handle(kernel_start)
     ev1 = None if kernel_stop is None else _event_handle(kernel_stop)
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode_append")
     st = lib().pa_decode_append(ctypes.byref(c), new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(),
                                 out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
                                 seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(),
@@ -534,6 +677,8 @@ def pa_decode_run(out, query, key_cache, value_cache, block_tables, seq_lens, sc
     if workspace is None:
         workspace = decode_workspace(query, key_cache, max_seq_len, partition_size)
     _need(workspace, "workspace")
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode_run")
     d = pa_decode_args()
     d.cache = ctypes.pointer(c)
     d.out, d.query = out.data_ptr(), query.data_ptr()
@@ -572,6 +717,10 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, cu_q_lens, seq_lens, bl
     T, Hq, D = query.shape
     if out.shape != query.shape or D != c.head_dim or cu_q_lens.shape[0] != S + 1 or block_tables.shape[0] != S:
         raise ValueError("shape mismatch between query/out/cu_q_lens/seq_lens/block_tables and the cache")
+    if debug_enabled():
+        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, block_tables.shape[1] * c.block_size,
+                           "pa_prefill_chunk")
+        debug_check_chunks(cu_q_lens, seq_lens, int(max_q_len), T, "pa_prefill_chunk")
     st = lib().pa_prefill_chunk(ctypes.byref(c), out.data_ptr(), query.data_ptr(), cu_q_lens.data_ptr(), seq_lens.data_ptr(),
                                 block_tables.data_ptr(), block_tables.shape[1], S, Hq, int(max_q_len), float(scale),
                                 _stream(stream))
@@ -586,6 +735,9 @@ def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
     _need(dst, "dst", torch.int32)
     if src.shape != dst.shape:
         raise ValueError("src and dst must have the same length")
+    if debug_enabled():
+        debug_check_blocks(src, c.num_blocks, "pa_copy_blocks")
+        debug_check_blocks(dst, c.num_blocks, "pa_copy_blocks", distinct=True, other=src)
     _check(lib().pa_copy_blocks(ctypes.byref(c), src.data_ptr(), dst.data_ptr(), src.numel(), _stream(stream)), "pa_copy_blocks")
 
 
@@ -602,6 +754,8 @@ def pa_gather_blocks(key_cache, value_cache, block_ids, key_out, value_out, stre
     n = block_ids.numel()
     _buf_ok(key_out, key_cache, n, "key_out")
     _buf_ok(value_out, value_cache, n, "value_out")
+    if debug_enabled():
+        debug_check_blocks(block_ids, c.num_blocks, "pa_gather_blocks")
     _check(lib().pa_gather_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_out.data_ptr(), value_out.data_ptr(),
                                   _stream(stream)), "pa_gather_blocks")
 
@@ -612,6 +766,8 @@ def pa_scatter_blocks(key_cache, value_cache, block_ids, key_in, value_in, strea
     n = block_ids.numel()
     _buf_ok(key_in, key_cache, n, "key_in")
     _buf_ok(value_in, value_cache, n, "value_in")
+    if debug_enabled():
+        debug_check_blocks(block_ids, c.num_blocks, "pa_scatter_blocks", distinct=True)
     _check(lib().pa_scatter_blocks(ctypes.byref(c), block_ids.data_ptr(), n, key_in.data_ptr(), value_in.data_ptr(),
                                    _stream(stream)), "pa_scatter_blocks")
 
