@@ -11,30 +11,32 @@
 // (ctx = seq_len - q_s; the chunk's own K/V are already in the pool) and
 // attends causally: position ctx+i sees keys 0 .. ctx+i.
 //
-// Work decomposition.  A workgroup of 4 waves (one per SIMD) owns 256 query
+// Work decomposition.  A workgroup of 8 waves (two per SIMD) owns 256 query
 // rows that share one KV head: the G heads of the group times 256/G
-// consecutive positions.  Each wave owns 64 rows as two halves of 32, so
-// every K or V operand read from LDS feeds two matrix products (LDS traffic
-// per flop is half that of 32-row waves).  Keys stream through in tiles of
-// 32; per wave and half
+// consecutive positions; each wave owns 32 of them.  Keys stream through in
+// tiles of 32; per wave
 //   S^T[32 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16 over D
 //   online softmax down each column (a column is one query row, held by a
 //   lane pair), P^T rounded to the storage type in registers
 //   O^T[D x 32 rows]     += V^T . P^T    v_mfma_f32_32x32x16 over the tile
-// With one wave per SIMD the matrix and vector work overlap inside the wave:
-// each iteration multiplies the scores of tile t+1 while it exponentiates
-// and rounds tile t's probabilities, then runs tile t's PV product while it
-// finds tile t+1's maxima and rescale factors.  Tiles whose keys need masks
-// (the causal diagonal, blocks missing from the pool), a rescale of the
-// accumulators, or the rounding remainder below take a slower, generic path.
+// Each step multiplies the scores of tile t+1 while it exponentiates and
+// rounds tile t's probabilities, then runs tile t's PV product while it
+// finds tile t+1's maxima and rescale factors; the two waves of a SIMD fill
+// each other's waits.  Masks (the causal diagonal, blocks missing from the
+// pool), the accumulator rescale and the rounding remainder below run only
+// on the tiles that need them.  A workgroup serves two query tiles of one
+// (sequence, KV head), j and n-1-j, so that every workgroup carries about
+// the same causal work.
 //
 // Staging.  Tiles move from the pool straight into LDS (16 bytes per lane,
-// no registers on the way), four stages deep: while tiles t and t+1 are
-// read, tile t+2 has landed and tile t+3 is in flight.  A stage holds the
-// tile's K as the pool stores it (column chunks of 32 dimensions, one
-// 64-byte row per key) and its V^T (one 64-byte row of 32 keys per
-// dimension); the 16-byte columns of row r are XOR-permuted by a function of
-// r's bits 1..3 so that the operand reads below hit every bank group once.
+// no registers on the way) through six stages, each its own array so that
+// the compiler waits only for the loads this code waits for.  A pass covers
+// two tiles between barriers: it starts the loads of tiles t+3 and t+4,
+// computes tiles t and t+1, and by its end those loads have landed.  A
+// stage holds the tile's K as the pool stores it (column chunks of 32
+// dimensions, one 64-byte row per key) and its V^T (one 64-byte row of 32
+// keys per dimension); the 16-byte columns of each row are permuted (kswz,
+// vswz) so that the operand reads hit every bank group once.
 //
 // Computing the transposed products keeps every operand a 16-byte LDS or
 // register read: the accumulator layout of S^T is directly the B operand of
