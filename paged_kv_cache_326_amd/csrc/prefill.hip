@@ -498,13 +498,13 @@ prefill_kernel(PrefillArgs a) {
       // A row that has seen no key yet (m_run = -inf) only holds masked
       // logits: exp2(-inf) = 0 with any finite reference.
       mref[hf] = m_new == -INFINITY ? 0.f : m_new;
-      l_run[hf] *= alpha[hf];
       moved = moved || move;
       // The row's largest probability in this tile against a lower bound of
-      // the row's sum including it: the sum so far (both lanes of the row)
-      // plus that probability.
+      // the row's sum including it: the sum so far (both lanes of the row,
+      // at the new reference; l_run itself is rescaled with the
+      // accumulators when the tile's step begins) plus that probability.
       const float pmax = fast_exp2(mt - mref[hf]);
-      split = split || pmax * (1.f - kShare) > kShare * sum_across_halves(l_run[hf]);
+      split = split || pmax * (1.f - kShare) > kShare * sum_across_halves(l_run[hf] * alpha[hf]);
     }
     split_next = __any(split);
     rescale = __any(moved);
@@ -611,17 +611,33 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) rescale_acc(o[hf][dt], alpha[hf]);
     }
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) l_run[hf] *= alpha[hf];
     u32x4 pb[kHalves][2];
     scores(Stage<st + 1>(), nxt);
     phase2(cur, mref, pb);
+    // Tile t's probabilities are formed here, beside tile t+1's score
+    // products, not sunk past the mask branch below to their first use.
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pb[hf][ks]));
+    if (tile_masked(t + 1, gaps)) mask(nxt, t + 1, gaps);
+    // Tile t's PV product and tile t+1's maxima share one stretch of code
+    // (no branch between them), so the vector work fills the matrix
+    // products' issue gaps; tile t's own split flag and reference are kept
+    // for its remainder product, which follows.
+    const bool split_cur = split;
+    float mref_cur[kHalves];
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) mref_cur[hf] = mref[hf];
     accumulate(S, pb);
-    if (split) {
+    phase1(nxt, alpha, mref, split, rescale);
+    if (split_cur) {
       u32x4 pl[kHalves][2];
-      remainders(cur, mref, pb, pl);
+      remainders(cur, mref_cur, pb, pl);
       accumulate(S, pl);
     }
-    if (tile_masked(t + 1, gaps)) mask(nxt, t + 1, gaps);
-    phase1(nxt, alpha, mref, split, rescale);
   };
 
   // A pass covers tiles t and t+1 (in stages S and S+1) between two
