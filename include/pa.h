@@ -40,7 +40,8 @@
  * slots) are the caller's contract; kernels nonetheless skip block IDs
  * outside [0, num_blocks), slots outside the pool, and clamp seq_lens to the
  * host-side bounds, so a bad table gives a wrong result, never an
- * out-of-bounds access.
+ * out-of-bounds access.  (The Python binding's PA_DEBUG=1 mode copies those
+ * contents to the host and rejects bad ones before each call.)
  *
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * num_heads / num_kv_heads in {1, 2, 4, 8}; dtype f32, f16, bf16
