@@ -354,6 +354,19 @@ def test_decode_max_length_sequence():
     _assert_close(_as64(out, w.dtype), ref, w.dtype, "max-length")
 
 
+@pytest.mark.parametrize("partition", [0, 1024])
+def test_decode_long_context_many_partitions(partition):
+    # A 131 072-token context beside two short sequences: 32 (automatic) or
+    # 128 partitions, ordered on the device, merged from that many partials.
+    w = synth.custom(seed=13, dtype="f16", num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                     seq_lens=[131072, 300, 1], pool_factor=1.0, poison_unused=False)
+    gw = harness.GpuWorkload(w)
+    out = gw.step(partition_size=partition)
+    _sync()
+    _, _, _, ref = harness.oracle_step(w)
+    _assert_close(_as64(out, w.dtype), ref, w.dtype, f"131072-token context, partition {partition}")
+
+
 def _relabel(w, seed):
     rng = np.random.default_rng(seed)
     perm = rng.permutation(w.num_blocks)
