@@ -262,9 +262,32 @@ decode_partition_kernel(DecodeArgs a) {
     // partitions first (partition-major), then each sequence's last, partial
     // one by decreasing size in eighths of a partition (and the partition 0
     // of empty sequences, which writes their zeros).  Ranks past the last
-    // unit exit at once: they come last in the grid, where they cost
-    // nothing.
+    // unit exit: they come last in the grid, behind all the work.
     const int lane = threadIdx.x & 63;
+    if ((int)(blockIdx.x / a.cache.num_kv_heads) >= a.num_seqs) {
+      // Every sequence has at least one unit, so ranks below the batch size
+      // always find one.  Past that, a bound on the number of units from the
+      // lengths read through the scalar cache (the sum of ceil(max(L, 1) / P)
+      // is at most the sum of max(L, 1), plus n (P - 1), over P) lets most
+      // workgroups past the end of the work leave without a vector load,
+      // which would queue behind the key and value streams of the
+      // workgroups still running (about 2 us on a 64-sequence batch whose
+      // grid is two-thirds such workgroups).
+      const int rank = (int)(blockIdx.x / a.cache.num_kv_heads);
+      const int n = a.num_seqs;
+      int64_t tot = (int64_t)n * (a.partition - 1);
+      auto len1 = [&](int v) -> int64_t {
+        v = v > a.max_seq_len ? a.max_seq_len : v;
+        return v < 1 ? 1 : v;
+      };
+      int i = 0;
+      for (; i + 16 <= n; i += 16) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tot += len1(a.seq_lens[i + j]);
+      }
+      for (; i < n; ++i) tot += len1(a.seq_lens[i]);
+      if (tot < (int64_t)(rank + 1) * a.partition) return;  // rank >= floor(tot / P) >= the unit count
+    }
     int Ls = lane < a.num_seqs ? a.seq_lens[lane] : -1;
     Ls = Ls < 0 ? (lane < a.num_seqs ? 0 : -1) : (Ls > a.max_seq_len ? a.max_seq_len : Ls);
     const int full = Ls > 0 ? Ls / a.partition : 0;

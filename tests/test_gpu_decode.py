@@ -292,6 +292,40 @@ def test_decode_device_order_covers_every_partition(num_seqs):
     _assert_close(got, ref, w.dtype, f"device-ordered decode, {num_seqs} sequences")
 
 
+@pytest.mark.parametrize("num_seqs", [17, 64])
+def test_decode_device_order_unit_bound_is_tight(num_seqs):
+    # Workgroups whose rank is at least the batch size first test it against
+    # a bound on the unit count, (sum of max(L, 1) + n (P - 1)) // P, and
+    # leave when past it.  With every length k P + 1 (or 0) the bound equals
+    # the count, so the last unit's workgroups sit right below it; 17
+    # sequences also take the lengths past the last whole 16.
+    rng = np.random.default_rng(500 + num_seqs)
+    P = 32
+    lens = np.asarray([int(k) * P + 1 for k in rng.integers(0, 7, num_seqs)], dtype=np.int32)
+    lens[0] = 6 * P + 1
+    lens[3] = 0
+    lens[-1] = 0
+    units = int(sum(max(1, -(-int(L) // P)) for L in lens))
+    assert (int(np.maximum(lens, 1).sum()) + num_seqs * (P - 1)) // P == units
+    w = synth.custom(seed=500 + num_seqs, dtype="bf16", num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                     seq_lens=[max(int(x), 1) for x in lens], pool_factor=1.2)
+    gw = harness.GpuWorkload(w)
+    gw.append()
+    _, kc, vc, _ = harness.oracle_step(w, seqs=[])
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    gw.seq_lens.copy_(torch.from_numpy(lens).to(gw.seq_lens.device))
+    gw.out.fill_(float("nan"))
+    pa.pa_decode_run(gw.out, gw.query, gw.key_cache, gw.value_cache, gw.block_tables, gw.seq_lens, w.scale,
+                     w.max_seq_len, partition_size=P)
+    _sync()
+    got = _as64(gw.out, w.dtype)
+    assert np.all(got[lens == 0] == 0)
+    ref = oracle.decode_attention(oracle.to_float64(w.query, w.dtype), kc, vc, w.block_tables, lens, w.scale)
+    _assert_close(got, ref, w.dtype, f"device-ordered decode at the unit bound, {num_seqs} sequences")
+
+
 @pytest.mark.parametrize("partition", [16, 32, 0])
 def test_decode_tiny_config_partitions(partition):
     w = synth.config(1)
