@@ -302,7 +302,7 @@ def key_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int
     """Shape of a key pool: each (block, KV head) tile's block_size rows cut
     into column chunks of 64 bytes of elements,
     [num_blocks, num_kv_heads, head_dim // kc, block_size, kc]."""
-    kc = 64 // torch.empty((), dtype=dtype).element_size()
+    kc = 64 // dtype.itemsize
     if head_dim % kc:
         raise ValueError(f"head_dim {head_dim} is not a multiple of the {kc}-element key chunk")
     return (num_blocks, num_kv_heads, head_dim // kc, block_size, kc)
@@ -611,16 +611,17 @@ def pa_decode_timed(out, query, key_cache, value_cache, block_tables, seq_lens, 
     return out
 
 
-def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, scale: float,
-                     max_seq_len: int, slot_mapping=None, workspace: Optional[torch.Tensor] = None,
-                     partition_size: int = 0, kernel_start=None, kernel_stop=None, stream=None, scales=None):
-    """One decode step: each sequence's new token (position seq_lens[s]-1)
-    written into the pool, then decode attention, in the partition kernel."""
+def _decode_append_call(out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, scale,
+                        max_seq_len, slot_mapping, workspace, partition_size, kernel_start, kernel_stop, stream, scales):
+    """Checks and marshals the arguments of pa_decode_append: returns the
+    pool descriptor (which the argument tuple points to), the tuple and the
+    slot mapping."""
     c = kv_cache(key_cache, value_cache, scales)
-    _need(query, "query", io_dtype(key_cache))
-    _need(out, "out", io_dtype(key_cache))
-    _need(new_key, "new_key", io_dtype(key_cache))
-    _need(new_value, "new_value", io_dtype(key_cache))
+    io = io_dtype(key_cache)
+    _need(query, "query", io)
+    _need(out, "out", io)
+    _need(new_key, "new_key", io)
+    _need(new_value, "new_value", io)
     _need(block_tables, "block_tables", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     S, Hq, D = query.shape
@@ -636,15 +637,57 @@ def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, blo
     _need(workspace, "workspace")
     ev0 = None if kernel_start is None else _event_handle(kernel_start)
     ev1 = None if kernel_stop is None else _event_handle(kernel_stop)
+    args = (ctypes.byref(c), new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(), out.data_ptr(),
+            query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), S, Hq,
+            int(max_seq_len), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            int(partition_size), ev0, ev1, _stream(stream))
+    return c, args, slot_mapping
+
+
+def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, scale: float,
+                     max_seq_len: int, slot_mapping=None, workspace: Optional[torch.Tensor] = None,
+                     partition_size: int = 0, kernel_start=None, kernel_stop=None, stream=None, scales=None):
+    """One decode step: each sequence's new token (position seq_lens[s]-1)
+    written into the pool, then decode attention, in the partition kernel."""
+    c, args, slot_mapping = _decode_append_call(out, query, key_cache, value_cache, new_key, new_value, block_tables,
+                                                seq_lens, scale, max_seq_len, slot_mapping, workspace, partition_size,
+                                                kernel_start, kernel_stop, stream, scales)
     if debug_enabled():
         debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len), "pa_decode_append")
-    st = lib().pa_decode_append(ctypes.byref(c), new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(),
-                                out.data_ptr(), query.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-                                seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), int(partition_size), ev0, ev1,
-                                _stream(stream))
-    _check(st, "pa_decode_append")
+    _check(lib().pa_decode_append(*args), "pa_decode_append")
     return slot_mapping
+
+
+def prepare_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens,
+                          scale: float, max_seq_len: int, slot_mapping=None, workspace: Optional[torch.Tensor] = None,
+                          partition_size: int = 0, kernel_start=None, kernel_stop=None, stream=None, scales=None):
+    """pa_decode_append with its arguments checked and marshalled once: the
+    returned function launches the step again on the same buffers (whose
+    contents, such as lengths, tables, queries and new rows, may change
+    between launches; the buffers themselves, the stream and max_seq_len may
+    not).  For a serving loop that keeps its step buffers in place, it takes
+    the binding's per-call work (about 15 us of Python) off the host's path
+    to the launch."""
+    c, args, slot_mapping = _decode_append_call(out, query, key_cache, value_cache, new_key, new_value, block_tables,
+                                                seq_lens, scale, max_seq_len, slot_mapping, workspace, partition_size,
+                                                kernel_start, kernel_stop, stream, scales)
+    keep = (c, out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, slot_mapping, workspace)
+    fn = lib().pa_decode_append
+    types = getattr(fn, "argtypes", None)
+    if types:  # numbers converted to their C types once, not on every call
+        args = tuple(t(a) if isinstance(a, (int, float)) else a for t, a in zip(types, args))
+    debug = debug_enabled()
+
+    def launch():
+        if debug:
+            debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len),
+                               "pa_decode_append")
+        st = fn(*args)
+        if st:
+            raise PaError(st, "pa_decode_append")
+
+    launch.buffers = keep  # the tensors the marshalled pointers refer to stay alive with the function
+    return launch
 
 
 def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int, device="cuda") -> torch.Tensor:

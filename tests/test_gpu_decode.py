@@ -202,6 +202,38 @@ def test_fused_append_decode_matches_append_then_decode(k, partition):
     _assert_close(_as64(gw.out, w.dtype), ref, w.dtype, f"fused append + decode, config {k}")
 
 
+@pytest.mark.parametrize("k,partition", [(1, 0), (3, 64)])
+def test_prepared_decode_append_matches_the_plain_call(k, partition):
+    # prepare_decode_append marshals the arguments once; its launches must
+    # match pa_decode_append bit for bit, also after the buffers' contents
+    # (queries, new rows) change in place between launches.
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    w = synth.config(k, scale_down=4 if k == 3 else 1)
+    ref, gw = harness.GpuWorkload(w), harness.GpuWorkload(w)
+    launch = pa.prepare_decode_append(gw.out, gw.query, gw.key_cache, gw.value_cache, gw.new_key, gw.new_value,
+                                      gw.block_tables, gw.seq_lens, w.scale, w.max_seq_len,
+                                      slot_mapping=gw.slot_mapping, partition_size=partition)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    for rnd in range(2):
+        if rnd:
+            for t in ("query", "new_key", "new_value"):
+                fresh = torch.randn(getattr(gw, t).shape, generator=g, device="cuda").to(getattr(gw, t).dtype)
+                getattr(gw, t).copy_(fresh)
+                getattr(ref, t).copy_(fresh)
+        pa.pa_decode_append(ref.out, ref.query, ref.key_cache, ref.value_cache, ref.new_key, ref.new_value,
+                            ref.block_tables, ref.seq_lens, w.scale, w.max_seq_len, slot_mapping=ref.slot_mapping,
+                            partition_size=partition)
+        gw.out.fill_(float("nan"))
+        launch()
+        _sync()
+        assert torch.equal(gw.slot_mapping, ref.slot_mapping)
+        for a_, b_ in ((gw.key_cache, ref.key_cache), (gw.value_cache, ref.value_cache), (gw.out, ref.out)):
+            assert np.array_equal(harness.from_device(a_, w.dtype).view(np.uint8),
+                                  harness.from_device(b_, w.dtype).view(np.uint8)), f"launch {rnd}"
+
+
 def _planned_vs_plain(w, partition=0, append=False):
     import torch
     from paged_kv_cache_326_amd import pa
