@@ -3,6 +3,8 @@
 // Sources: [P1] "大模型推理内存优化从 KV Cache 分页到连续批处理的工程实践",
 // section "KV Cache 的内存开销与分页机制" (block table maps logical to
 // physical blocks; a new token goes into the current block or a new one).
+#include <algorithm>
+
 #include "pa_common.h"
 #include "pa_launch.h"
 
@@ -187,35 +189,188 @@ __global__ void __launch_bounds__(kScatterThreads) reshape_and_cache_kernel(Scat
   scatter_group<T>(a, t0, n, [&](int i) { return slots[t0 + i]; });
 }
 
-// Slot mapping and scatter in one pass.  Workgroup (x, s) covers new tokens
-// x*kGroup .. of sequence s: the slot of each comes from the block table
-// (and is recorded in slots[]), and its rows are scattered as above.
+// Slot mapping and scatter in one pass, by tiles.  The new tokens of one
+// sequence occupy consecutive positions, so those that fall into one
+// logical block share its physical block and fill consecutive rows of its
+// key tile and consecutive columns of its value tile.  One workgroup per
+// (block touched by a sequence's new tokens, KV head): it computes the
+// block's slots (recorded by the head-0 workgroup), copies the tokens' key
+// rows into the key tile (each wave writing runs of whole 64-byte chunk
+// rows), and transposes their values through LDS into the value tile,
+// writing each tile row's covered part in 16-byte pieces.  A prefill chunk
+// that fills a block thus writes both tiles of every (block, KV head) whole
+// and contiguous.
+//
+// Which block: for batches of at most 64 sequences every workgroup reads
+// all the chunk lengths (one per lane) and numbers the (sequence, block)
+// pairs in order, so the grid needs only an upper bound on their count,
+// (num_tokens + n (2B - 2)) / B; larger batches take a grid of (block
+// slot k, sequence, head), k slowest, whose slots past a sequence's blocks
+// leave at once.  Workgroups that find no block cost their launch, and in a
+// batch of long chunks and one-token steps those launches were most of the
+// time (7.5 of 12.4 us for the (k, sequence, head) grid on 4 chunks of 512
+// and 48 steps).
+constexpr int kAppendSeqs = 64;           // sequences numbered by one wave
+constexpr int kMaxTileWords = 32 * 128;   // one value tile of 32-bit source words at most (32 x 128)
+
 template <typename T>
 __global__ void __launch_bounds__(kScatterThreads) append_kernel(
     ScatterArgs<T> a, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q_lens, int64_t* __restrict__ slots,
-    int32_t num_tokens) {
-  const int s = blockIdx.y;
-  const int tq = cu_q_lens[s];
-  const int q = cu_q_lens[s + 1] - tq;
-  const int L = seq_lens[s];
-  const int first = blockIdx.x * kGroup;
-  // Tokens outside the list are not touched.
-  const int64_t t0 = (int64_t)tq + first;
-  int64_t n64 = q - first < kGroup ? q - first : kGroup;
-  if (n64 > num_tokens - t0) n64 = num_tokens - t0;
-  if (n64 <= 0 || t0 < 0) return;
-  const int n = (int)n64;
-  // The slot is recorded as computed (a block id outside the pool gives a
-  // slot past the pool, which the scatter skips).
-  scatter_group<T>(a, t0, n, [&](int i) -> int64_t {
-    const int pos = L - q + first + i;
-    int64_t slot = -1;
-    if (pos >= 0 && pos / a.block_size < max_blocks)
-      slot = (int64_t)block_tables[(int64_t)s * max_blocks + pos / a.block_size] * a.block_size + pos % a.block_size;
-    slots[t0 + i] = slot;
-    return slot;
-  });
+    int32_t num_tokens, int32_t num_seqs, int32_t numbered) {
+  using S = typename Src<T>::type;
+  constexpr int VEC = vec16<S>();             // source elements per 16-byte chunk
+  constexpr int KC = key_chunk<T>();          // elements per 64-byte key chunk
+  constexpr int CPC = KC / VEC;               // source chunks per key chunk
+  constexpr int PE = 16 / Elem<T>::kBytes;    // value-tile elements per 16-byte piece
+  constexpr int SW = sizeof(S) == 4 ? 1 : 2;  // source elements per 32-bit word
+  constexpr int kItems = kMaxTileWords / 4 / kScatterThreads;  // 16-byte items per thread at most
+  static_assert(KC % VEC == 0, "a source chunk lies inside one key chunk");
+  __shared__ uint32_t s_v[kMaxTileWords];
+  const int H = a.num_kv_heads, D = a.head_dim, B = a.block_size;
+  const int tid = threadIdx.x;
+  const int h = (int)(blockIdx.x % H);
+  int s, k, tq, q, L;
+  if (numbered) {
+    // Blocks touched by sequence l's chunk: positions L - q .. L - 1.
+    const int lane = tid & 63;
+    int nb = 0, tl = 0, ql = 0, Ll = 0;
+    if (lane < num_seqs) {
+      tl = cu_q_lens[lane];
+      ql = cu_q_lens[lane + 1] - tl;
+      Ll = seq_lens[lane];
+      const int64_t pl = (int64_t)Ll - ql;
+      if (ql > 0) {
+        const int64_t first = pl >= 0 ? pl / B : -((-pl + B - 1) / B);
+        const int64_t last = (pl + ql - 1) >= 0 ? (pl + ql - 1) / B : -((-(pl + ql - 1) + B - 1) / B);
+        nb = (int)(last - first + 1);
+      }
+    }
+    // Inclusive prefix sum over the lanes.
+    int incl = nb;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int y = __shfl_up(incl, d, 64);
+      incl += lane >= d ? y : 0;
+    }
+    const int r = (int)(blockIdx.x / H);
+    const uint64_t past = __ballot(incl <= r);  // sequences wholly before pair r
+    s = __builtin_popcountll(past);
+    if (s >= num_seqs) return;  // past the last pair
+    s = __builtin_amdgcn_readfirstlane(s);
+    k = r - (s > 0 ? __builtin_amdgcn_readlane(incl, s - 1) : 0);
+    tq = __builtin_amdgcn_readlane(tl, s);
+    q = __builtin_amdgcn_readlane(ql, s);
+    L = __builtin_amdgcn_readlane(Ll, s);
+  } else {
+    const int sk = (int)(blockIdx.x / H);
+    s = sk % num_seqs;
+    k = sk / num_seqs;
+    tq = cu_q_lens[s];
+    q = cu_q_lens[s + 1] - tq;
+    L = seq_lens[s];
+  }
+  if (q <= 0) return;
+  // Positions pf .. pf+q-1 (token rows tq ..); this workgroup takes the
+  // k-th block they touch, j, clipped to the token rows that exist.
+  const int64_t pf = (int64_t)L - q;
+  const int64_t j = (pf >= 0 ? pf / B : -((-pf + B - 1) / B)) + k;
+  int64_t lo = pf > j * B ? pf : j * B;
+  int64_t hi = pf + q < (j + 1) * B ? pf + q : (j + 1) * B;
+  const int64_t t_lo = tq + (lo - pf);
+  if (t_lo < 0) lo -= t_lo;
+  if (tq + (hi - pf) > num_tokens) hi -= tq + (hi - pf) - num_tokens;
+  if (lo >= hi) return;
+  const int n = (int)(hi - lo);
+  const int64_t t0 = tq + (lo - pf);  // token row of position lo
+  const int o0 = (int)(lo - j * B);   // its row of the tile
+  const bool in_table = j >= 0 && j < max_blocks;
+  const int64_t phys = in_table ? (int64_t)block_tables[(int64_t)s * max_blocks + j] : -1;
+
+  // Every source load of the segment is issued before anything is stored
+  // (a store into the pool could alias a source row as far as the compiler
+  // knows) and without waiting for the table entry.  Key items it = (chunk
+  // c, token o, piece sub), sub fastest, so a wave stores whole chunk rows
+  // of consecutive tokens; value items (token o, piece ch) as the rows lie.
+  const int cpr = D / VEC;
+  const int nk = n * cpr;
+  u32x4 kx[kItems], vx[kItems];
+#pragma unroll
+  for (int b = 0; b < kItems; ++b) {
+    const int it = tid + b * kScatterThreads;
+    if (it < nk) {
+      const int sub = it % CPC, o = (it / CPC) % n, c = it / (CPC * n);
+      kx[b] = *reinterpret_cast<const u32x4*>(a.key + ((t0 + o) * H + h) * D + (c * CPC + sub) * VEC);
+      vx[b] = *reinterpret_cast<const u32x4*>(a.value + ((t0 + it / cpr) * H + h) * D + (it % cpr) * VEC);
+    }
+  }
+  // The values staged in LDS as they come ([token][dim], D / SW words a
+  // row) for the transposed writes below.
+  const int W = D / SW;
+#pragma unroll
+  for (int b = 0; b < kItems; ++b) {
+    const int it = tid + b * kScatterThreads;
+    if (it < nk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_v[(it / cpr) * W + (it % cpr) * 4 + e] = vx[b][e];
+    }
+  }
+  if (h == 0) {
+    for (int i = tid; i < n; i += kScatterThreads) slots[t0 + i] = in_table ? phys * B + o0 + i : -1;
+  }
+  if (!in_table || phys < 0 || phys * B >= a.pool_slots) return;  // not written
+#pragma unroll
+  for (int b = 0; b < kItems; ++b) {
+    const int it = tid + b * kScatterThreads;
+    if (it < nk) {
+      const int sub = it % CPC, o = (it / CPC) % n, c = it / (CPC * n);
+      store_kv_chunk<T>(a.key_cache, a.value_cache, 0, phys, o0 + o, h, c * CPC + sub, VEC, H, D, B, kx[b],
+                        a.k_scale, a.v_scale);
+    }
+  }
+  __syncthreads();
+  // Piece p of value-tile row d holds tokens p*PE .. p*PE+PE-1 of the block.
+  const int p0 = o0 / PE, p1 = (o0 + n - 1) / PE;
+  const int npc = p1 - p0 + 1;
+  T* tile = a.value_cache + (phys * H + h) * (int64_t)D * B;
+  for (int it = tid; it < D * npc; it += kScatterThreads) {
+    const int p = p0 + it % npc, d = it / npc;
+    T* row = tile + (int64_t)d * B;
+    // Source element (token o of the block, dim d) as raw bits (16-bit
+    // types in the low half).
+    auto elem = [&](int o) -> uint32_t {
+      const uint32_t w = s_v[(o - o0) * W + d / SW];
+      return SW == 1 ? w : (w >> (16 * (d % 2))) & 0xffffu;
+    };
+    const int e0 = p * PE;
+    if (e0 >= o0 && e0 + PE <= o0 + n) {
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if constexpr (Elem<T>::kBytes == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = elem(e0 + e);
+      } else if constexpr (Elem<T>::kBytes == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = elem(e0 + 2 * e) | (elem(e0 + 2 * e + 1) << 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r[e / 4] |= f32_to_e4m3(f16_lo(elem(e0 + e)) / a.v_scale) << (8 * (e % 4));
+      }
+      *reinterpret_cast<u32x4*>(row + e0) = r;
+    } else {
+      for (int e = 0; e < PE; ++e) {
+        const int o = e0 + e;
+        if (o < o0 || o >= o0 + n) continue;
+        const uint32_t bits = elem(o);
+        if constexpr (Elem<T>::kBytes == 4) {
+          reinterpret_cast<uint32_t*>(row)[o] = bits;
+        } else if constexpr (Elem<T>::kBytes == 2) {
+          reinterpret_cast<uint16_t*>(row)[o] = (uint16_t)bits;
+        } else {
+          reinterpret_cast<uint8_t*>(row)[o] = (uint8_t)f32_to_e4m3(f16_lo(bits) / a.v_scale);
+        }
+      }
+    }
+  }
 }
 
 template <typename T>
@@ -240,9 +395,20 @@ static hipError_t launch_append_t(const KvCacheArgs& c, const void* key, const v
                                   const int32_t* cu_q_lens, int32_t num_seqs, int32_t max_q_len, int64_t* slots,
                                   int32_t num_tokens, hipStream_t stream) {
   if (num_seqs == 0 || max_q_len == 0) return hipSuccess;
-  dim3 grid((max_q_len + kGroup - 1) / kGroup, num_seqs);
-  hipLaunchKernelGGL(append_kernel<T>, grid, dim3(kScatterThreads), 0, stream, scatter_args<T>(c, key, value),
-                     block_tables, max_blocks, seq_lens, cu_q_lens, slots, num_tokens);
+  const int tile_words = c.block_size * c.head_dim / (sizeof(typename Src<T>::type) == 4 ? 1 : 2);
+  if (tile_words > kMaxTileWords) return hipErrorInvalidValue;
+  // (sequence, block) pairs: numbered on the device for small batches,
+  // else every sequence's chunk may touch up to ceil((B - 1 + q) / B)
+  // blocks.
+  const int B = c.block_size;
+  const bool numbered = num_seqs <= kAppendSeqs;
+  const int64_t pairs = numbered ? ((int64_t)num_tokens + (int64_t)num_seqs * (2 * B - 2)) / B
+                                 : ((int64_t)max_q_len + 2 * B - 2) / B * num_seqs;
+  const int64_t groups = pairs * c.num_kv_heads;
+  if (groups > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_kernel<T>, dim3((unsigned)groups), dim3(kScatterThreads), 0, stream,
+                     scatter_args<T>(c, key, value), block_tables, max_blocks, seq_lens, cu_q_lens, slots, num_tokens,
+                     num_seqs, (int32_t)numbered);
   return hipGetLastError();
 }
 

@@ -479,11 +479,14 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, strea
     _check(st, "pa_reshape_and_cache")
 
 
-def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len: int,
-                 slot_mapping=None, stream=None, scales=None):
+def _append_kv_call(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len, slot_mapping,
+                    stream, scales):
+    """Checks and marshals the arguments of pa_append_kv: returns the pool
+    descriptor, the argument tuple and the slot mapping."""
     c = kv_cache(key_cache, value_cache, scales)
-    _need(key, "key", io_dtype(key_cache))
-    _need(value, "value", io_dtype(key_cache))
+    io = io_dtype(key_cache)
+    _need(key, "key", io)
+    _need(value, "value", io)
     _need(block_tables, "block_tables", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(cu_q_lens, "cu_q_lens", torch.int32)
@@ -494,15 +497,57 @@ def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_
     if slot_mapping is None:
         slot_mapping = torch.empty(T, dtype=torch.int64, device=key.device)
     _need(slot_mapping, "slot_mapping", torch.int64)
+    args = (ctypes.byref(c), key.data_ptr(), value.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+            seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, int(max_q_len), slot_mapping.data_ptr(), T, _stream(stream))
+    return c, args, slot_mapping
+
+
+def _debug_append(c, key, block_tables, seq_lens, cu_q_lens, max_q_len):
+    debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, block_tables.shape[1] * c.block_size,
+                       "pa_append_kv")
+    debug_check_chunks(cu_q_lens, seq_lens, int(max_q_len), key.shape[0], "pa_append_kv")
+
+
+def pa_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len: int,
+                 slot_mapping=None, stream=None, scales=None):
+    c, args, slot_mapping = _append_kv_call(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens,
+                                            max_q_len, slot_mapping, stream, scales)
     if debug_enabled():
-        debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, block_tables.shape[1] * c.block_size,
-                           "pa_append_kv")
-        debug_check_chunks(cu_q_lens, seq_lens, int(max_q_len), T, "pa_append_kv")
-    st = lib().pa_append_kv(ctypes.byref(c), key.data_ptr(), value.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-                            seq_lens.data_ptr(), cu_q_lens.data_ptr(), S, int(max_q_len), slot_mapping.data_ptr(), T,
-                            _stream(stream))
-    _check(st, "pa_append_kv")
+        _debug_append(c, key, block_tables, seq_lens, cu_q_lens, max_q_len)
+    _check(lib().pa_append_kv(*args), "pa_append_kv")
     return slot_mapping
+
+
+def _prepared(name, args, keep, check):
+    """A function that calls library entry point `name` again with the
+    arguments marshalled once (numbers converted to their C types here)."""
+    fn = getattr(lib(), name)
+    types = getattr(fn, "argtypes", None)
+    if types:
+        args = tuple(t(a) if isinstance(a, (int, float)) else a for t, a in zip(types, args))
+    debug = debug_enabled()
+
+    def launch():
+        if debug:
+            check()
+        st = fn(*args)
+        if st:
+            raise PaError(st, name)
+
+    launch.buffers = keep  # the tensors the marshalled pointers refer to stay alive with the function
+    return launch
+
+
+def prepare_append_kv(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, max_q_len: int,
+                      slot_mapping=None, stream=None, scales=None):
+    """pa_append_kv with its arguments checked and marshalled once (see
+    prepare_decode_append): the returned function launches it again on the
+    same buffers."""
+    c, args, slot_mapping = _append_kv_call(key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens,
+                                            max_q_len, slot_mapping, stream, scales)
+    keep = (c, key_cache, value_cache, key, value, block_tables, seq_lens, cu_q_lens, slot_mapping)
+    return _prepared("pa_append_kv", args, keep,
+                     lambda: _debug_append(c, key, block_tables, seq_lens, cu_q_lens, max_q_len))
 
 
 def pa_decode_auto_partition(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int) -> int:
@@ -672,22 +717,9 @@ def prepare_decode_append(out, query, key_cache, value_cache, new_key, new_value
                                                 seq_lens, scale, max_seq_len, slot_mapping, workspace, partition_size,
                                                 kernel_start, kernel_stop, stream, scales)
     keep = (c, out, query, key_cache, value_cache, new_key, new_value, block_tables, seq_lens, slot_mapping, workspace)
-    fn = lib().pa_decode_append
-    types = getattr(fn, "argtypes", None)
-    if types:  # numbers converted to their C types once, not on every call
-        args = tuple(t(a) if isinstance(a, (int, float)) else a for t, a in zip(types, args))
-    debug = debug_enabled()
-
-    def launch():
-        if debug:
-            debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len),
-                               "pa_decode_append")
-        st = fn(*args)
-        if st:
-            raise PaError(st, "pa_decode_append")
-
-    launch.buffers = keep  # the tensors the marshalled pointers refer to stay alive with the function
-    return launch
+    return _prepared("pa_decode_append", args, keep,
+                     lambda: debug_check_tables(block_tables, seq_lens, c.num_blocks, c.block_size, int(max_seq_len),
+                                                "pa_decode_append"))
 
 
 def decode_plan(seq_lens_host, max_seq_len: int, partition_size: int, device="cuda") -> torch.Tensor:

@@ -1,5 +1,6 @@
-"""The prepared decode step (prepare_decode_append) checks its arguments the
-way pa_decode_append does, once, before anything reaches the library (CPU)."""
+"""The prepared calls (prepare_decode_append, prepare_append_kv) check their
+arguments the way the plain calls do, once, before anything reaches the
+library (CPU)."""
 
 import pytest
 import torch
@@ -29,3 +30,10 @@ def test_key_chunk_follows_the_element_size():
         assert pa.key_shape(5, 2, 16, 128, dt) == (5, 2, 128 // kc, 16, kc)
     with pytest.raises(ValueError, match="not a multiple"):
         pa.key_shape(5, 2, 16, 48, torch.float16)
+
+
+def test_prepared_append_refuses_host_tensors():
+    a = _args()
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        pa.prepare_append_kv(a["key_cache"], a["value_cache"], a["new_key"], a["new_value"], a["block_tables"],
+                             a["seq_lens"], torch.zeros(4, dtype=torch.int32), 1)
