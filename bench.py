@@ -475,6 +475,33 @@ def fp8_decode_only(steps: int, warmup: int, copies_n: int, partition: int = 0):
     }
 
 
+def scatter_only(steps: int, warmup: int, copies_n: int):
+    """The mixed batch's scatter of its 2096 new tokens alone, for counter
+    collection on the two scatter kernels: pa_append_kv (slots from the
+    tables, `append_kernel`) and pa_reshape_and_cache with the same slots
+    (`reshape_and_cache_kernel`), each through prepared or plain calls in
+    bursts.  One JSON line with the mean call times and the rate on the
+    algorithmic bytes (K and V rows read and written, slots written)."""
+    from paged_kv_cache_326_amd import pa, synth
+
+    w = synth.config(5, poison_unused=False)
+    cs = _copies(w, copies_n)
+    mq = int(w.q_lens.max())
+    appends = [pa.prepare_append_kv(c.key_cache, c.value_cache, c.new_key, c.new_value, c.block_tables, c.seq_lens,
+                                    c.cu_q_lens, mq, c.slot_mapping) for c in cs]
+    for i in range(warmup):
+        appends[i % len(appends)]()
+    ta = _burst_us(lambda i: appends[i % len(appends)](), iters=steps)
+    tr = _burst_us(lambda i: cs[i % len(cs)].scatter(), iters=steps)
+    nb = 4 * w.num_new_tokens * w.num_kv_heads * w.head_dim * w.elem_bytes + 8 * w.num_new_tokens
+    return {
+        "workload": synth.CONFIG_NAMES[5] + "_scatter", "tokens": w.num_new_tokens, "algorithmic_bytes": nb,
+        "append_kv_us": round(ta, 2), "append_kv_frac_of_hbm_peak": round(nb / ta / 1e3 / HBM_PEAK_GBS, 4),
+        "reshape_and_cache_us": round(tr, 2), "steps": steps,
+        "note": "reshape_and_cache through plain binding calls, whose host time (about 9 us) can exceed the kernel's",
+    }
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """Time the oracle (as it stands) on this host: scatter + decode of the
     whole batch, repeated until `budget_s` has elapsed (at least once)."""
@@ -570,6 +597,8 @@ def main():
                     help="time only the mixed config's chunked prefill (for counter collection)")
     ap.add_argument("--fp8-decode", action="store_true",
                     help="time only the benchmark layer's decode over FP8 pools (for counter collection)")
+    ap.add_argument("--scatter", action="store_true",
+                    help="time only the mixed batch's scatter of its new tokens (for counter collection)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="instead: time a plain streaming read of the benchmark layer's bytes at several launch shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -615,6 +644,9 @@ def main():
         return
     if args.fp8_decode:
         print(json.dumps(fp8_decode_only(args.steps, args.warmup, args.copies, args.partition)), flush=True)
+        return
+    if args.scatter:
+        print(json.dumps(scatter_only(args.steps, args.warmup, args.copies)), flush=True)
         return
     if args.stream_ceiling:
         nb = algorithmic_decode_bytes(synth.config(2, poison_unused=False))
