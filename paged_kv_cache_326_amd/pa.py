@@ -711,8 +711,9 @@ def prepare_decode_append(out, query, key_cache, value_cache, new_key, new_value
     contents, such as lengths, tables, queries and new rows, may change
     between launches; the buffers themselves, the stream and max_seq_len may
     not).  For a serving loop that keeps its step buffers in place, it takes
-    the binding's per-call work (about 15 us of Python) off the host's path
-    to the launch."""
+    the binding's per-call checks (more than 10 us of Python) off the host's
+    path to the launch.  PA_DEBUG is read once, here: with it set, every
+    launch checks the tables first."""
     c, args, slot_mapping = _decode_append_call(out, query, key_cache, value_cache, new_key, new_value, block_tables,
                                                 seq_lens, scale, max_seq_len, slot_mapping, workspace, partition_size,
                                                 kernel_start, kernel_stop, stream, scales)
