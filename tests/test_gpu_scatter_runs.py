@@ -224,3 +224,37 @@ def test_prepared_append_matches_the_plain_call():
         assert torch.equal(gw.slot_mapping, ref.slot_mapping)
         assert np.array_equal(_pool_bytes(gw.key_cache), _pool_bytes(ref.key_cache)), f"launch {rnd}"
         assert np.array_equal(_pool_bytes(gw.value_cache), _pool_bytes(ref.value_cache)), f"launch {rnd}"
+
+
+@pytest.mark.parametrize("dt,H", [("bf16", 1), ("f16", 16), ("fp8", 16), ("f32", 3)])
+def test_scatters_across_kv_head_counts(dt, H):
+    # Both scatters take one KV head per workgroup: one head, many heads and
+    # a count that is not a power of two, through pa_append_kv (chunks and
+    # one-token steps) and pa_reshape_and_cache (the same tokens to random
+    # distinct slots).
+    import torch
+    from paged_kv_cache_326_amd import pa
+
+    q_lens = [40, 1, 17, 1, 33]
+    ctx = [5, 60, 16, 0, 31]
+    w = synth.custom(seed=700 + H, dtype="f16" if dt == "fp8" else dt, num_heads=H, num_kv_heads=H, head_dim=64,
+                     block_size=16, seq_lens=[c + q for c, q in zip(ctx, q_lens)], q_lens=q_lens, pool_factor=2.0)
+    scales = FP8_SCALES if dt == "fp8" else None
+    gw = harness.GpuWorkload(w)
+    kc, vc = _gpu_pool(gw, dt)
+    pa.pa_append_kv(kc, vc, gw.new_key, gw.new_value, gw.block_tables, gw.seq_lens, gw.cu_q_lens, max(q_lens),
+                    gw.slot_mapping, scales=scales)
+    ref_slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.q_lens, w.block_size)
+    np.testing.assert_array_equal(gw.slot_mapping.cpu().numpy(), ref_slots)
+    ek, ev = _expected(w, ref_slots, dt)
+    assert np.array_equal(_pool_bytes(kc), ek)
+    assert np.array_equal(_pool_bytes(vc), ev)
+
+    rng = np.random.default_rng(H)
+    slots = rng.permutation(w.num_blocks * w.block_size)[:w.num_new_tokens].astype(np.int64)
+    gw2 = harness.GpuWorkload(w)
+    kc2, vc2 = _gpu_pool(gw2, dt)
+    pa.pa_reshape_and_cache(kc2, vc2, gw2.new_key, gw2.new_value, torch.from_numpy(slots).cuda(), scales=scales)
+    ek2, ev2 = _expected(w, slots, dt)
+    assert np.array_equal(_pool_bytes(kc2), ek2)
+    assert np.array_equal(_pool_bytes(vc2), ev2)
